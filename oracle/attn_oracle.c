@@ -1,0 +1,160 @@
+/*
+ * Plain fp64 CPU oracle for exact softmax attention (forward).
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or load
+ * this file or the library built from it; only the test suite, the smoke check
+ * and the benchmark's CPU-baseline leg do. It shares no code with the HIP path.
+ *
+ * What it computes (the definition, written out, no tiling and no online update):
+ *   For one (batch, head) slice with Q in R^{Nq x d}, K, V in R^{Nk x d} and a
+ *   positive scale s:
+ *       x_ij = sum_c Q[i,c] K[j,c]                  raw score, S = Q K^T
+ *       P_i. = softmax over the valid keys j of s*x_ij
+ *       O_i. = sum_j P_ij V[j,.]
+ *       LSE_i = ln sum_{valid j} exp(s*x_ij)
+ *   Sources: "用 CuTe 读懂 FlashAttention" (blog.qingsen.net), the notation block
+ *   that defines S = QK^T, P = softmax_row(sS), O = PV, s = 1/sqrt(D), and its final
+ *   section ("最后：归一化并写回 O"), which defines LSE = s*m + log(l) with m the
+ *   raw (unscaled) row maximum and checks it against log(sum(exp(s*S))); "CUDA
+ *   算子工程" ch. 14 §14.1 (the scaled dot-product definition).
+ *
+ * Safe softmax in three passes over the stored score row (max, exponential sum,
+ * weighted sum of V), as the pwwt.cn FlashAttention-forward notes §3.1 and
+ * ch. 14 §14.2 describe the naive softmax. With z_j = s*x_j and m = max z_j,
+ *   l = sum exp(z_j - m),  O = (sum exp(z_j - m) V_j) / l,  LSE = m + ln l,
+ * which equals s*m_raw + ln l of the blog's final section because s > 0.
+ *
+ * Causal masking is top-left aligned: key j is valid for query i iff j <= i
+ * (the blog's causal section, Fig. 11). With that alignment key 0 is valid for
+ * every query, so a row can have no valid key only when Nk = 0; such a row gets
+ * O = 0 and LSE = -inf (the limit of an empty sum; the pages leave the case open).
+ *
+ * Arithmetic: IEEE double, libm exp/log, compiled without fast-math, so the
+ * sums are evaluated strictly in loop order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* One output row. z is caller scratch of length Nk. Returns nothing; writes
+ * o_row[0..d) and *lse_out. */
+static void oracle_one_row(const double* q_row, const double* k, const double* v,
+                           int64_t Nk, int64_t d, double scale, int causal, int64_t i,
+                           double* z, double* o_row, double* lse_out) {
+  int64_t nvalid = Nk;
+  if (causal) nvalid = (i + 1 < Nk) ? (i + 1) : Nk;   /* keys 0..i are valid */
+  if (nvalid <= 0) {
+    for (int64_t c = 0; c < d; ++c) o_row[c] = 0.0;
+    *lse_out = -INFINITY;
+    return;
+  }
+  /* scores z_j = s * (q . k_j) over the valid keys */
+  for (int64_t j = 0; j < nvalid; ++j) {
+    const double* k_row = k + j * d;
+    double x = 0.0;
+    for (int64_t c = 0; c < d; ++c) x += q_row[c] * k_row[c];
+    z[j] = scale * x;
+  }
+  /* pass 1: row maximum */
+  double m = z[0];
+  for (int64_t j = 1; j < nvalid; ++j)
+    if (z[j] > m) m = z[j];
+  /* pass 2: sum of exponentials relative to the maximum */
+  double l = 0.0;
+  for (int64_t j = 0; j < nvalid; ++j) l += exp(z[j] - m);
+  /* pass 3: normalised weights times V */
+  for (int64_t c = 0; c < d; ++c) o_row[c] = 0.0;
+  for (int64_t j = 0; j < nvalid; ++j) {
+    double p = exp(z[j] - m) / l;
+    const double* v_row = v + j * d;
+    for (int64_t c = 0; c < d; ++c) o_row[c] += p * v_row[c];
+  }
+  *lse_out = m + log(l);
+}
+
+static int oracle_check_args(const void* q, const void* k, const void* v, const void* o,
+                             const void* lse, int64_t BH, int64_t Nq, int64_t Nk, int64_t d,
+                             double scale) {
+  if (BH < 0 || Nq < 0 || Nk < 0 || d < 0) return 2;
+  if (!(scale > 0.0) || !isfinite(scale)) return 3;
+  if (BH * Nq == 0) return 0;
+  if (!q || !o || !lse) return 1;
+  if (Nk > 0 && (!k || !v)) return 1;
+  return 0;
+}
+
+/* Full forward over every row.
+ * q: [BH, Nq, d], k, v: [BH, Nk, d], o: [BH, Nq, d], lse: [BH, Nq]; all row-major
+ * contiguous doubles, owned by the caller. Returns 0 on success, 1 for a null
+ * pointer, 2 for a negative size, 3 for a scale that is not finite and > 0,
+ * 4 when scratch memory cannot be allocated. */
+int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, double* o,
+                        double* lse, int64_t BH, int64_t Nq, int64_t Nk, int64_t d,
+                        double scale, int causal) {
+  int rc = oracle_check_args(q, k, v, o, lse, BH, Nq, Nk, d, scale);
+  if (rc || BH * Nq == 0) return rc;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+    if (!z) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 8)
+      for (int64_t r = 0; r < BH * Nq; ++r) {
+        int64_t bh = r / Nq, i = r % Nq;
+        oracle_one_row(q + r * d, k + bh * Nk * d, v + bh * Nk * d, Nk, d, scale, causal, i, z,
+                       o + r * d, lse + r);
+      }
+      free(z);
+    }
+  }
+  return fail ? 4 : 0;
+}
+
+/* Selected rows only. rows[t] is a flat row index bh*Nq + i in [0, BH*Nq);
+ * o_rows: [nrows, d], lse_rows: [nrows]. Same return codes, plus 5 for a row
+ * index out of range. */
+int oracle_attn_rows_f64(const double* q, const double* k, const double* v, int64_t BH,
+                         int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
+                         const int64_t* rows, int64_t nrows, double* o_rows, double* lse_rows) {
+  int rc = oracle_check_args(q, k, v, o_rows, lse_rows, BH, Nq, Nk, d, scale);
+  if (rc) return rc;
+  if (nrows <= 0) return 0;
+  if (!rows) return 1;
+  for (int64_t t = 0; t < nrows; ++t)
+    if (rows[t] < 0 || rows[t] >= BH * Nq) return 5;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+    if (!z) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 4)
+      for (int64_t t = 0; t < nrows; ++t) {
+        int64_t r = rows[t];
+        int64_t bh = r / Nq, i = r % Nq;
+        oracle_one_row(q + r * d, k + bh * Nk * d, v + bh * Nk * d, Nk, d, scale, causal, i, z,
+                       o_rows + t * d, lse_rows + t);
+      }
+      free(z);
+    }
+  }
+  return fail ? 4 : 0;
+}
+
+/* Number of threads the parallel regions above use. */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
