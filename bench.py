@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact attention forward (fa_fwd) on one MI355X.
+
+A step is one fa_fwd call over the whole batch of the headline workload
+(B=2, H=16, N=4096, d=64, fp16, non-causal, scale 1/8): the complete hot path
+(Q-tile pinning, K/V streaming, both MFMA GEMMs, online softmax, masking,
+epilogue). Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line. ``value`` is TFLOP/s counting 4*B*H*N^2*d (halved for causal).
+``roofline`` prices the kernel against the dense fp16/bf16 MFMA peak, using the
+per-launch duration measured with HIP events on the stream the kernel runs on.
+``cpu_baseline`` times the fp64 CPU oracle on the same inputs (rank 0, N=1 only).
+The other workloads are timed briefly and reported under ``other_workloads``.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+MFMA_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk/CU (dense fp16/bf16) x 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+HEADLINE = 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=HEADLINE, help="1..5 (default: the headline 2)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true")
+    ap.add_argument("--traffic", type=str, default=None,
+                    help="JSON file with measured per-launch HBM bytes {workload: bytes}")
+    return ap.parse_args()
+
+
+def time_workload(w, steps, warmup):
+    import torch
+    import exact_attention_forward_fwd_amd as fa
+    from exact_attention_forward_fwd_amd.workloads import make_inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v, _ = make_inputs(w)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    tile = w.tile or (None, None)
+
+    def step():
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, block_m=tile[0], block_n=tile[1],
+               out=o, lse=lse, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # events bracket every launch on the kernel's own stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_all0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    total_ms = t_all0.elapsed_time(t_all1)
+    return dict(ms_per_step=total_ms / steps, kernel_ms_avg=sum(per) / len(per),
+                kernel_ms_median=per[len(per) // 2], kernel_ms_min=per[0],
+                wall_ms_per_step=(wall1 - wall0) * 1e3 / steps,
+                inputs=(q, k, v))
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The fp64 oracle on this workload's inputs: whole (b, h) slices, in order, until
+    the budget is spent (at least one slice)."""
+    import numpy as np
+    import oracle
+    from exact_attention_forward_fwd_amd.workloads import make_inputs
+
+    q, k, v, _ = make_inputs(w)
+    q = q.double().numpy(); k = k.double().numpy(); v = v.double().numpy()
+    q = q.reshape(-1, w.N, w.d); k = k.reshape(-1, w.N, w.d); v = v.reshape(-1, w.N, w.d)
+    slices = 0
+    t0 = time.perf_counter()
+    # time one slice first to size the sample
+    while slices < q.shape[0]:
+        oracle.attention_fwd(q[slices], k[slices], v[slices], w.scale, w.causal)
+        slices += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = w.flops / (w.B * w.H) * slices
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{slices} of {w.B * w.H} (batch, head) slices of {w.label()}, every row, "
+                      f"fp64 three-pass C oracle, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
+              "multi-GPU mode (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import exact_attention_forward_fwd_amd as fa
+    from exact_attention_forward_fwd_amd.workloads import WORKLOADS
+
+    fa.load_library()
+    w = WORKLOADS[args.workload]
+    r = time_workload(w, args.steps, args.warmup)
+    tflops = w.flops / (r["ms_per_step"] * 1e-3) / 1e12
+    achieved = w.flops / (r["kernel_ms_avg"] * 1e-3) / 1e12
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        traffic = json.load(open(args.traffic)).get(str(w.index))
+    out = {
+        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, halved for causal) and % of MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) Q, K, V; no dataset)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": w.scale, "tile": list(w.tile) if w.tile else None,
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * tflops / MFMA_PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel_ms_avg": round(r["kernel_ms_avg"], 5),
+                     "kernel_ms_median": round(r["kernel_ms_median"], 5)},
+    }
+    del r
+    if not args.no_others:
+        others = []
+        for idx in sorted(WORKLOADS):
+            if idx == w.index:
+                continue
+            wo = WORKLOADS[idx]
+            ro = time_workload(wo, max(5, args.steps // 5), max(2, args.warmup // 2))
+            tf = wo.flops / (ro["kernel_ms_avg"] * 1e-3) / 1e12
+            others.append({"workload": wo.name, "dtype": wo.dtype, "causal": wo.causal,
+                           "kernel_ms_avg": round(ro["kernel_ms_avg"], 5),
+                           "tflops": round(tf, 2), "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS, 4)})
+            del ro
+            torch.cuda.empty_cache()
+        out["other_workloads"] = others
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+"""ctypes binding of libfa.so: the same entry points as include/fa.h, argument
+marshalling only. Every step of the attention forward runs in the HIP kernels of
+the library; there is no fallback of any kind. If the library is missing or fails
+to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+
+FA_F16 = 0
+FA_BF16 = 1
+
+STATUS_NAMES = {
+    0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED_HEADDIM",
+    4: "FA_ERR_BAD_SCALE", 5: "FA_ERR_BAD_DTYPE", 6: "FA_ERR_MISALIGNED", 7: "FA_ERR_TOO_LARGE",
+    8: "FA_ERR_UNSUPPORTED_TILE", 9: "FA_ERR_HIP",
+}
+EXPORTED = ("fa_fwd", "fa_fwd_tiled", "fa_tile_supported", "fa_default_tile", "fa_status_str")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_str(status)})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libfa.so and declare the C signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run exact_attention_forward_fwd_amd.build.build() "
+                           "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    common = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp]
+    lib.fa_fwd.argtypes = common
+    lib.fa_fwd.restype = i32
+    lib.fa_fwd_tiled.argtypes = common + [i32, i32]
+    lib.fa_fwd_tiled.restype = i32
+    lib.fa_tile_supported.argtypes = [i64, i32, i32]
+    lib.fa_tile_supported.restype = i32
+    lib.fa_default_tile.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.fa_default_tile.restype = i32
+    lib.fa_status_str.argtypes = [i32]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().fa_status_str(int(status)).decode()
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream) -> int:
+    """Raw C call; pointers are integers (device addresses). Returns the fa_status."""
+    return load_library().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, int(causal), dtype, stream)
+
+
+def fa_fwd_tiled(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream, block_m, block_n) -> int:
+    return load_library().fa_fwd_tiled(q, k, v, o, lse, B, H, N, d, scale, int(causal), dtype,
+                                       stream, block_m, block_n)
+
+
+def fa_tile_supported(d: int, block_m: int, block_n: int) -> bool:
+    return bool(load_library().fa_tile_supported(d, block_m, block_n))
+
+
+def fa_default_tile(B: int, H: int, N: int, d: int, causal: bool):
+    bm, bn = ctypes.c_int(0), ctypes.c_int(0)
+    st = load_library().fa_default_tile(B, H, N, d, int(causal), ctypes.byref(bm), ctypes.byref(bn))
+    if st != 0:
+        raise FaError(st, "fa_default_tile")
+    return bm.value, bn.value
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return FA_F16
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    raise TypeError(f"dtype must be float16 or bfloat16, got {t.dtype}")
+
+
+def fwd(q, k, v, scale: float | None = None, causal: bool = False, block_m: int | None = None,
+        block_n: int | None = None, out=None, lse=None, stream=None):
+    """Attention forward on torch tensors [B, H, N, d] (contiguous, same device/dtype).
+
+    Returns (o, lse): o like q, lse float32 [B, H, N]. ``scale`` defaults to 1/sqrt(d).
+    Runs asynchronously on ``stream`` (default: torch's current stream).
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, d]")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape [B, H, N, d]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    B, H, N, d = q.shape
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+            float(scale), causal, dt, sp)
+    if block_m is None and block_n is None:
+        st = fa_fwd(*args)
+    else:
+        st = fa_fwd_tiled(*args, int(block_m), int(block_n))
+    if st != 0:
+        raise FaError(st, "fa_fwd")
+    return out, lse

@@ -1,0 +1,441 @@
+// Exact attention forward (FlashAttention-2 loop order) for MI355X / gfx950 (CDNA4).
+//
+// One workgroup owns BM query rows of one (batch, head) slice; each of its BM/32
+// waves owns 32 of them. The workgroup streams K and V in tiles of BN keys
+// through LDS. Per tile, every wave
+//   1. computes S^T = K_tile Q_w^T on v_mfma_f32_32x32x16_{f16,bf16} (fp32 acc):
+//      with the keys as MFMA rows and the queries as columns, each lane ends up
+//      holding one query's scores for 16 keys of every 32-key block, so the
+//      row (per-query) reductions are 15 in-lane ops plus one permlane32 swap;
+//   2. masks the causal diagonal / ragged tail to -inf (only on tiles that need it);
+//   3. updates the online-softmax state in registers: m' = max(m, rowmax), the
+//      weights P = 2^(c x - c m') with c = s log2(e) folded into one FMA,
+//      alpha = 2^(c m - c m'), l' = alpha l + rowsum P, U' = alpha U;
+//   4. rounds P to 16 bits in registers; those registers are directly the B
+//      operand of O^T += V^T P^T (the key order inside each 16-key MFMA step is
+//      permuted identically on both operands, which a sum over keys allows);
+//   5. reads V^T fragments with ds_read_b64_tr_b16 (transposing 16-bit LDS reads).
+// After the last tile: O = U / l, LSE = ln2 (fl(c m) + log2 l), written once.
+//
+// The method is that of "用 CuTe 读懂 FlashAttention" (blog.qingsen.net): one block
+// pins a Q tile and walks the K/V tiles (its opening example and step 1), the
+// online-softmax state and recurrence of step 4, P kept in registers as the second
+// GEMM's operand (step 5), whole-tile skipping plus element masking for causal
+// (causal section) and the single final normalisation with the LSE side output
+// (final section); loop order and the -inf guard follow "CUDA 算子工程" ch. 14
+// §14.5. Register/LDS layout, the transposed-Q formulation and the instruction
+// choices are this file's own, made for CDNA4's 64-wide waves and MFMA shapes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+#include "fa.h"
+
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <bool BF16> struct Elem;
+template <> struct Elem<false> { using vec8 = f16x8; };
+template <> struct Elem<true> { using vec8 = bf16x8; };
+
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma_32x32x16(i16x8 a, i16x8 b, f32x16 c) {
+  using V = typename Elem<BF16>::vec8;
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(V, a), __builtin_bit_cast(V, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(V, a), __builtin_bit_cast(V, b), c, 0, 0, 0);
+}
+
+// Round two fp32 values to 16 bits (round-to-nearest-even) and pack them.
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  if constexpr (BF16) {
+    __bf16 a = (__bf16)x, b = (__bf16)y;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  } else {
+    _Float16 a = (_Float16)x, b = (_Float16)y;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+}
+
+// Reductions across the two 32-lane halves of a wave. v_permlane32_swap with the
+// same register as both operands leaves the low half's value in every lane of r[0]
+// and the high half's value in every lane of r[1].
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ i16x4 ds_read_tr16(const short* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) short*)lds_ptr));
+}
+
+struct Params {
+  const short* q;
+  const short* k;
+  const short* v;
+  short* o;
+  float* lse;
+  int N;
+  int num_m_blocks;   // ceil(N / BM)
+  int total_wgs;      // B * H * num_m_blocks
+  float c;            // scale * log2(e)
+};
+
+template <int D, bool BF16, bool CAUSAL, int BM, int BN>
+__global__ __launch_bounds__(BM * 2) void fa_fwd_kernel(Params p) {
+  // Every fused multiply-add below is written out; the compiler must not fuse the
+  // rounded reference products into neighbouring adds (see the softmax state note).
+#pragma clang fp contract(off)
+  constexpr int NW = BM / 32;          // waves per workgroup
+  constexpr int NT = NW * 64;          // threads per workgroup
+  constexpr int KP = D + 8;            // K tile LDS row pitch (elements): rows shift by 16 B
+  constexpr int VP = D + 32;           // V tile LDS row pitch (elements): rows shift by 64 B
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  constexpr int PER_T = BN * CPR / NT; // chunks of each of K and V loaded per thread per tile
+  static_assert(BM % 32 == 0 && BN % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert((BN * CPR) % NT == 0, "loader must divide evenly");
+
+  __shared__ __attribute__((aligned(16))) short lds_k[BN * KP];
+  __shared__ __attribute__((aligned(16))) short lds_v[BN * VP];
+
+  // Workgroups are dispatched to the 8 XCDs round-robin (blockIdx % 8). Give each
+  // XCD a contiguous range of work items so that the query blocks of one head
+  // share that XCD's L2 while they stream the same K and V.
+  const int bid = blockIdx.x;
+  const int T = p.total_wgs;
+  const int xcd = bid & 7, slot = bid >> 3, per = T >> 3, rem = T & 7;
+  const int w = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int bh = w / p.num_m_blocks;
+  int mb = w - bh * p.num_m_blocks;
+  if (CAUSAL) mb = p.num_m_blocks - 1 - mb;   // longest rows first
+  const int N = p.N;
+  const int m0 = mb * BM;
+  const int64_t head = (int64_t)bh * N * D;
+  const short* __restrict__ qh = p.q + head;
+  const short* __restrict__ kh = p.k + head;
+  const short* __restrict__ vh = p.v + head;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int wq0 = m0 + wave * 32;          // first query of this wave
+  const int qrow = wq0 + l32;              // this lane's query
+  const float c = p.c;
+
+  // Q^T as the B operand, kept in registers for the whole loop:
+  // qf[ks] = Q[qrow][16 ks + 8 hi .. +7].
+  i16x8 qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    if (qrow < N)
+      qf[ks] = *(const i16x8*)(qh + (int64_t)qrow * D + ks * 16 + 8 * hi);
+    else
+      qf[ks] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+
+  f32x16 acc_o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
+  // Softmax state of this lane's query. The weights of every tile are taken
+  // relative to ref = fl(c * m), the product rounded once, and ref itself is kept:
+  // alpha = 2^(ref_old - ref_new) is then exactly 1 whenever the maximum did not
+  // change. Using the exact c*m_old against the rounded c*m_new instead would
+  // scale l and U by 2^(rounding error) on every tile and drift LSE over long rows.
+  float m_run = -INFINITY;    // running raw-score maximum
+  float ref_run = -INFINITY;  // fl(c * m_run)
+  float l_run = 0.f;          // this lane's share of the exponential sum
+
+  const int n_end = CAUSAL ? min(N, m0 + BM) : N;
+  const int ntiles = (n_end + BN - 1) / BN;
+
+  i16x8 kreg[PER_T], vreg[PER_T];
+  auto gload = [&](int n0) {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int ch = tid + i * NT;
+      const int row = ch / CPR, col = (ch % CPR) * 8;
+      if (n0 + row < N) {
+        kreg[i] = *(const i16x8*)(kh + (int64_t)(n0 + row) * D + col);
+        vreg[i] = *(const i16x8*)(vh + (int64_t)(n0 + row) * D + col);
+      } else {
+        // keys past N: K is masked anyway, V must be finite zeros (0 * garbage may be NaN)
+        kreg[i] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        vreg[i] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+      const int ch = tid + i * NT;
+      const int row = ch / CPR, col = (ch % CPR) * 8;
+      *(i16x8*)(lds_k + row * KP + col) = kreg[i];
+      *(i16x8*)(lds_v + row * VP + col) = vreg[i];
+    }
+  };
+
+  if (ntiles > 0) gload(0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int n0 = t * BN;
+    __syncthreads();                 // everyone is done reading the previous tile
+    lstore();
+    if (t + 1 < ntiles) gload(n0 + BN);  // next tile's loads overlap this tile's math
+    __syncthreads();
+    if (CAUSAL && n0 > wq0 + 31) continue;   // whole tile in this wave's future
+
+    // ---- S^T = K_tile Q^T ----
+    f32x16 s[BN / 32];
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const i16x8 a = *(const i16x8*)(lds_k + (kb * 32 + l32) * KP + ks * 16 + 8 * hi);
+        s[kb] = mfma_32x32x16<BF16>(a, qf[ks], s[kb]);
+      }
+    }
+    // s[kb][r] is the raw score of query qrow and key n0 + kb*32 + 8(r/4) + 4 hi + r%4.
+
+    // ---- masks: causal diagonal and ragged tail ----
+    const bool need_mask = (n0 + BN > N) || (CAUSAL && n0 + BN - 1 > wq0);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax ----
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float ref_new = m_new * c;
+    // -inf guard: while a row has seen no valid key, use 0 as the exponent base
+    const float base = (m_new == -INFINITY) ? 0.f : ref_new;
+    const float neg_cm = -base;
+    const float alpha = __builtin_amdgcn_exp2f(ref_run - base);
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, neg_cm));
+        s[kb][r] = e;
+        rs += e;
+      }
+    l_run = __builtin_fmaf(l_run, alpha, rs);
+    m_run = m_new;
+    ref_run = ref_new;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+
+    // ---- P^T as 16-bit B operands: step tt covers s[tt/2][8 (tt%2) .. +7] ----
+    i16x8 pf[BN / 16];
+#pragma unroll
+    for (int tt = 0; tt < BN / 16; ++tt) {
+      const int kb = tt >> 1, base = 8 * (tt & 1);
+      uint32_t w0 = pack2<BF16>(s[kb][base + 0], s[kb][base + 1]);
+      uint32_t w1 = pack2<BF16>(s[kb][base + 2], s[kb][base + 3]);
+      uint32_t w2 = pack2<BF16>(s[kb][base + 4], s[kb][base + 5]);
+      uint32_t w3 = pack2<BF16>(s[kb][base + 6], s[kb][base + 7]);
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      pf[tt] = __builtin_bit_cast(i16x8, (u32x4){w0, w1, w2, w3});
+    }
+
+    // ---- O^T += V^T P^T ----
+    // Lane (group of 16 = g, index i) of a ds_read_b64_tr_b16 receives
+    // element j from the lane 4j + i/4 of its group, component i%4. With lane L of
+    // the group pointing at V[key0 + L/4][dcol0 + 4 (L%4)], lane i gets
+    // V[key0 + j][dcol0 + i], j = 0..3: four consecutive keys of one d column.
+    const int tr_row = 4 * hi + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int tt = 0; tt < BN / 16; ++tt) {
+        const int key0 = (tt >> 1) * 32 + 16 * (tt & 1) + tr_row;
+        const short* src = lds_v + key0 * VP + db * 32 + tr_col;
+        const i16x4 a0 = ds_read_tr16(src);
+        const i16x4 a1 = ds_read_tr16(src + 8 * VP);
+        const i16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc_o[db] = mfma_32x32x16<BF16>(a, pf[tt], acc_o[db]);
+      }
+    }
+  }
+
+  // ---- epilogue: O = U / l, LSE = ln2 (ref + log2 l) with ref = fl(c m) ----
+  const float l_tot = sum_halves(l_run);
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if (qrow < N) {
+    short* orow = p.o + head + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // acc_o[db][4g + e] holds O^T[d = 32 db + 8 g + 4 hi + e][qrow]
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        u32x2 pk;
+        pk[0] = pack2<BF16>(acc_o[db][4 * g + 0] * inv, acc_o[db][4 * g + 1] * inv);
+        pk[1] = pack2<BF16>(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv);
+        *(u32x2*)(orow + db * 32 + 8 * g + 4 * hi) = pk;
+      }
+    if (hi == 0) {
+      const float lse = (l_tot > 0.f) ? kLn2 * (ref_run + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
+      p.lse[(int64_t)bh * N + qrow] = lse;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Host side
+// ------------------------------------------------------------------------------------
+
+struct TileShape { int bm, bn; };
+constexpr TileShape kTiles[] = {{64, 64}, {128, 64}};
+
+template <int D, bool BF16, bool CAUSAL, int BM, int BN>
+hipError_t launch_one(const Params& p, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, BM, BN>), dim3(p.total_wgs), dim3(BM * 2), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16, bool CAUSAL>
+hipError_t launch_tile(const Params& p, int bm, int bn, hipStream_t stream) {
+  if (bm == 64 && bn == 64) return launch_one<D, BF16, CAUSAL, 64, 64>(p, stream);
+  if (bm == 128 && bn == 64) return launch_one<D, BF16, CAUSAL, 128, 64>(p, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_d(const Params& p, bool bf16, bool causal, int bm, int bn, hipStream_t stream) {
+  if (bf16) return causal ? launch_tile<D, true, true>(p, bm, bn, stream) : launch_tile<D, true, false>(p, bm, bn, stream);
+  return causal ? launch_tile<D, false, true>(p, bm, bn, stream) : launch_tile<D, false, false>(p, bm, bn, stream);
+}
+
+bool tile_ok(int64_t d, int bm, int bn) {
+  if (d != 64 && d != 128) return false;
+  for (const TileShape& t : kTiles)
+    if (t.bm == bm && t.bn == bn) return true;
+  return false;
+}
+
+fa_status validate(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                   int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_BAD_DTYPE;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
+  if (N >= ((int64_t)1 << 31) / d) return FA_ERR_TOO_LARGE;   // N*d must fit int32 offsets
+  return FA_OK;
+}
+
+fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+              int64_t N, int64_t d, float scale, int causal, fa_dtype dtype, void* stream, int bm, int bn) {
+  fa_status st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!tile_ok(d, bm, bn)) return FA_ERR_UNSUPPORTED_TILE;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  const int64_t mblocks = (N + bm - 1) / bm;
+  if (B >= ((int64_t)1 << 31) || H >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
+  if (B * H >= ((int64_t)1 << 31) / mblocks + 1) return FA_ERR_TOO_LARGE;
+  Params p;
+  p.q = (const short*)q;
+  p.k = (const short*)k;
+  p.v = (const short*)v;
+  p.o = (short*)o;
+  p.lse = lse;
+  p.N = (int)N;
+  const int64_t total = B * H * mblocks;
+  if (total >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
+  p.num_m_blocks = (int)mblocks;
+  p.total_wgs = (int)total;
+  p.c = (float)((double)scale * 1.4426950408889634);  // s * log2(e), rounded once
+  const hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dtype == FA_BF16;
+  hipError_t e = (d == 64) ? launch_d<64>(p, bf16, causal != 0, bm, bn, s)
+                           : launch_d<128>(p, bf16, causal != 0, bm, bn, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+void default_tile(int64_t N, int* bm, int* bn) {
+  *bm = (N <= 128) ? 64 : 128;
+  *bn = 64;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                 int64_t H, int64_t N, int64_t d, float scale, int causal, fa_dtype dtype,
+                 void* stream) {
+  int bm, bn;
+  default_tile(N, &bm, &bn);
+  return run(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream, bm, bn);
+}
+
+fa_status fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                       int64_t H, int64_t N, int64_t d, float scale, int causal, fa_dtype dtype,
+                       void* stream, int block_m, int block_n) {
+  return run(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream, block_m, block_n);
+}
+
+int fa_tile_supported(int64_t d, int block_m, int block_n) { return tile_ok(d, block_m, block_n) ? 1 : 0; }
+
+fa_status fa_default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int* block_m,
+                          int* block_n) {
+  (void)B; (void)H; (void)causal;
+  if (!block_m || !block_n) return FA_ERR_NULL_PTR;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  default_tile(N, block_m, block_n);
+  return FA_OK;
+}
+
+const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL_PTR: return "null pointer";
+    case FA_ERR_BAD_SHAPE: return "negative B, H or N";
+    case FA_ERR_UNSUPPORTED_HEADDIM: return "head dimension must be 64 or 128";
+    case FA_ERR_BAD_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_BAD_DTYPE: return "dtype must be FA_F16 or FA_BF16";
+    case FA_ERR_MISALIGNED: return "q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_TOO_LARGE: return "problem too large (N*d >= 2^31 or grid >= 2^31)";
+    case FA_ERR_UNSUPPORTED_TILE: return "tile shape not compiled";
+    case FA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) exact attention forward library (libfa.so).
+ *
+ * One call computes, for every (batch b, head h) slice of contiguous tensors,
+ *     S = Q K^T,  P = softmax_row(s S),  O = P V,  LSE_i = ln sum_j exp(s S_ij)
+ * with the FlashAttention-2 loop order: a workgroup keeps one block of query rows
+ * on chip, streams blocks of K and V, updates the per-row online-softmax state
+ * (running raw maximum m, sum l, unnormalised numerator U rescaled by
+ * alpha = exp(s (m - m'))) and normalises once at the end. S and P never reach
+ * device memory.
+ *
+ * Sources for the operation: "用 CuTe 读懂 FlashAttention：一次 forward 的完整流程"
+ * (blog.qingsen.net) — the notation block (S, P, O, s = 1/sqrt(D)), step 4 (the
+ * online-softmax state and recurrence), the causal section (top-left alignment,
+ * Fig. 11) and the final section (O = U / l, LSE = s m + log l); "CUDA 算子工程"
+ * ch. 14 §14.5 (FA2 forward: inputs Q, K, V in [N, d], outputs O in [N, d] and
+ * LSE in [N]).
+ *
+ * Every entry point is a plain C function; no C++ or framework type crosses it.
+ * Functions return a status code and never throw, print or abort.
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V and O. */
+typedef enum {
+  FA_F16 = 0,  /* IEEE binary16 */
+  FA_BF16 = 1  /* bfloat16 */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL_PTR = 1,           /* a required pointer is NULL */
+  FA_ERR_BAD_SHAPE = 2,          /* B, H or N negative */
+  FA_ERR_UNSUPPORTED_HEADDIM = 3,/* d is not 64 or 128 */
+  FA_ERR_BAD_SCALE = 4,          /* scale is not finite or not > 0 */
+  FA_ERR_BAD_DTYPE = 5,          /* dtype is not FA_F16 / FA_BF16 */
+  FA_ERR_MISALIGNED = 6,         /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
+  FA_ERR_TOO_LARGE = 7,          /* N*d >= 2^31 elements, or the grid exceeds 2^31-1 workgroups */
+  FA_ERR_UNSUPPORTED_TILE = 8,   /* (block_m, block_n) not among the compiled tile shapes */
+  FA_ERR_HIP = 9                 /* the HIP runtime reported an error at launch */
+} fa_status;
+
+/*
+ * fa_fwd — exact attention forward, asynchronous on `stream`.
+ *
+ *   q, k, v : device pointers to [B, H, N, d] contiguous tensors of `dtype`
+ *             (row-major; element (b,h,i,c) at ((b*H + h)*N + i)*d + c). Read only.
+ *   o       : device pointer to a [B, H, N, d] contiguous tensor of `dtype`; fully
+ *             overwritten. Must not overlap q, k or v.
+ *   lse     : device pointer to a [B, H, N] contiguous float32 tensor; fully
+ *             overwritten with ln sum_{valid j} exp(scale * q_i . k_j).
+ *   B, H, N : batch, heads, sequence length (queries and keys alike). N need not
+ *             be a multiple of any tile size.
+ *   d       : head dimension, 64 or 128.
+ *   scale   : the softmax scale s (the caller passes 1/sqrt(d) for standard
+ *             attention; there is no default at this level). Finite and > 0.
+ *   causal  : nonzero masks key j > query i (top-left alignment, j <= i valid).
+ *   dtype   : FA_F16 or FA_BF16. Scores, softmax state and accumulators are fp32;
+ *             the softmax weights are rounded to `dtype` (round-to-nearest-even)
+ *             for the P·V product and O is rounded to `dtype` at the end.
+ *   stream  : a hipStream_t (NULL = the default stream).
+ *
+ * Ownership: the caller allocates and frees every buffer. The library allocates
+ * nothing, keeps no state between calls and does not synchronise; the call
+ * returns once the kernel is enqueued. A device fault surfaces at the caller's
+ * next synchronisation. B*H*N == 0 is a no-op that returns FA_OK.
+ * Errors: arguments are validated before anything is launched; on any status
+ * other than FA_OK nothing was enqueued (FA_ERR_HIP: the launch itself failed).
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                 fa_dtype dtype, void* stream);
+
+/*
+ * fa_fwd_tiled — fa_fwd with an explicit tile shape: block_m query rows per
+ * workgroup and block_n keys per K/V tile (fa_fwd picks these itself). Used for
+ * testing and tuning. Supported shapes are reported by fa_tile_supported; any
+ * other pair returns FA_ERR_UNSUPPORTED_TILE without launching.
+ */
+fa_status fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                       fa_dtype dtype, void* stream, int block_m, int block_n);
+
+/* 1 if (block_m, block_n) is compiled for head dimension d, else 0. */
+int fa_tile_supported(int64_t d, int block_m, int block_n);
+
+/* The tile shape fa_fwd would choose for these arguments (written to *block_m,
+ * *block_n); returns FA_OK, or FA_ERR_UNSUPPORTED_HEADDIM / FA_ERR_NULL_PTR. */
+fa_status fa_default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                          int* block_m, int* block_n);
+
+/* Static description of a status code. Never NULL. */
+const char* fa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */

@@ -1,0 +1,97 @@
+"""The C-ABI library loads, exports every function include/fa.h declares, and its
+argument validation answers without touching a GPU (no compute calls here: every
+call below is rejected, or is an empty problem, before anything is launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_forward_fwd_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(fa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared_functions():
+        assert name in exported, name
+
+
+def test_status_strings():
+    for code in range(10):
+        s = fa.status_str(code)
+        assert s and s != "unknown status"
+    assert fa.status_str(99) == "unknown status"
+
+
+def test_tile_queries():
+    assert fa.fa_tile_supported(64, 64, 64) and fa.fa_tile_supported(128, 128, 64)
+    assert not fa.fa_tile_supported(96, 64, 64) and not fa.fa_tile_supported(64, 48, 64)
+    assert fa.fa_default_tile(1, 1, 128, 64, False) == (64, 64)
+    bm, bn = fa.fa_default_tile(2, 16, 4096, 64, False)
+    assert fa.fa_tile_supported(64, bm, bn)
+    with pytest.raises(fa.FaError):
+        fa.fa_default_tile(1, 1, 128, 80, False)
+
+
+# Fake, aligned, never-dereferenced addresses: validation rejects before any launch.
+A = 0x10000
+
+
+def call(q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=64, d=64, scale=0.125, causal=0, dtype=0):
+    return fa.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+def test_validation_codes_without_gpu():
+    assert call(q=None) == 1 and call(lse=None) == 1 and call(o=None) == 1
+    assert call(B=-1) == 2 and call(N=-5) == 2
+    assert call(d=96) == 3 and call(d=0) == 3
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(scale=s) == 4
+    assert call(dtype=2) == 5 and call(dtype=-1) == 5
+    assert call(q=A + 8) == 6 and call(o=A + 2) == 6 and call(lse=A + 2) == 6
+    assert call(N=1 << 25) == 7                       # N*d >= 2^31 with d = 64
+    assert call(B=1 << 20, H=1 << 20, N=1 << 10) == 7  # grid too large
+    assert fa.fa_fwd_tiled(A, A, A, A, A, 1, 1, 64, 64, 0.1, 0, 0, None, 96, 64) == 8
+
+
+def test_empty_problems_need_no_pointers():
+    assert call(q=None, k=None, v=None, o=None, lse=None, N=0) == 0
+    assert call(q=None, k=None, v=None, o=None, lse=None, B=0) == 0
+    assert call(q=None, k=None, v=None, o=None, lse=None, H=0, causal=1) == 0
+
+
+def test_product_path_does_not_reference_the_oracle():
+    """The HIP library and the binding never load or import the CPU oracle."""
+    pkg = os.path.dirname(fa.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "liboracle" not in text, f
+    out = subprocess.run(["nm", "-D", fa.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "oracle" not in out
+
+
+def test_missing_library_raises(tmp_path):
+    with pytest.raises(RuntimeError):
+        fa.load_library(str(tmp_path / "libfa.so"))
