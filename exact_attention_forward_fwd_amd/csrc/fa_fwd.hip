@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+#include <type_traits>
 
 #include "fa.h"
 
@@ -52,18 +53,6 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(i16x8 a, i16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(V, a), __builtin_bit_cast(V, b), c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(V, a), __builtin_bit_cast(V, b), c, 0, 0, 0);
-}
-
-// Round two fp32 values to 16 bits (round-to-nearest-even) and pack them.
-template <bool BF16>
-__device__ __forceinline__ uint32_t pack2(float x, float y) {
-  if constexpr (BF16) {
-    __bf16 a = (__bf16)x, b = (__bf16)y;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-  } else {
-    _Float16 a = (_Float16)x, b = (_Float16)y;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-  }
 }
 
 // Reductions across the two 32-lane halves of a wave. v_permlane32_swap with the
@@ -96,19 +85,41 @@ struct Params {
   float c;            // scale * log2(e)
 };
 
-template <int D, bool BF16, bool CAUSAL, int BM, int BN>
-__global__ __launch_bounds__(BM * 2) void fa_fwd_kernel(Params p) {
+// Exponent headroom (log2 units) before the softmax reference is moved. The
+// weights of a tile are 2^(c x - ref) with ref = fl(c m_ref); keeping ref while the
+// running maximum stays within TAU of it leaves every weight <= 2^TAU (256, far
+// inside fp16's range) and skips the rescale of l and U on almost every tile. The
+// final O = U / l and LSE = ln2 (ref + log2 l) hold for any common reference.
+constexpr float kTau = 8.0f;
+
+// Buffer resource over [base, base + bytes): loads at offsets past the end return
+// zeros, which pads the ragged last key/query tile without any branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ i16x8 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// NW waves per workgroup; each wave owns QB blocks of 32 queries (BM = 32 NW QB
+// query rows per workgroup) and shares every K and V fragment it reads from LDS
+// across those QB blocks.
+template <int D, bool BF16, bool CAUSAL, int NW, int QB, int BN>
+__global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   // Every fused multiply-add below is written out; the compiler must not fuse the
   // rounded reference products into neighbouring adds (see the softmax state note).
 #pragma clang fp contract(off)
-  constexpr int NW = BM / 32;          // waves per workgroup
+  constexpr int BM = 32 * NW * QB;     // query rows per workgroup
   constexpr int NT = NW * 64;          // threads per workgroup
   constexpr int KP = D + 8;            // K tile LDS row pitch (elements): rows shift by 16 B
   constexpr int VP = D + 32;           // V tile LDS row pitch (elements): rows shift by 64 B
   constexpr int CPR = D / 8;           // 16-byte chunks per row
   constexpr int PER_T = BN * CPR / NT; // chunks of each of K and V loaded per thread per tile
-  static_assert(BM % 32 == 0 && BN % 32 == 0 && D % 32 == 0, "tile shape");
+  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
   static_assert((BN * CPR) % NT == 0, "loader must divide evenly");
+  using f32x2 = float __attribute__((ext_vector_type(2)));
+  using e16x2 = typename std::conditional<BF16, __bf16 __attribute__((ext_vector_type(2))),
+                                          _Float16 __attribute__((ext_vector_type(2)))>::type;
 
   __shared__ __attribute__((aligned(16))) short lds_k[BN * KP];
   __shared__ __attribute__((aligned(16))) short lds_v[BN * VP];
@@ -126,59 +137,59 @@ __global__ __launch_bounds__(BM * 2) void fa_fwd_kernel(Params p) {
   const int N = p.N;
   const int m0 = mb * BM;
   const int64_t head = (int64_t)bh * N * D;
-  const short* __restrict__ qh = p.q + head;
-  const short* __restrict__ kh = p.k + head;
-  const short* __restrict__ vh = p.v + head;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;   // < 2^32: the host checks N*d < 2^31
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head, head_bytes);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int wq0 = m0 + wave * 32;          // first query of this wave
-  const int qrow = wq0 + l32;              // this lane's query
+  const int wq0 = m0 + wave * 32 * QB;     // first query of this wave
   const float c = p.c;
 
   // Q^T as the B operand, kept in registers for the whole loop:
-  // qf[ks] = Q[qrow][16 ks + 8 hi .. +7].
-  i16x8 qf[D / 16];
+  // qf[qb][ks] = Q[wq0 + 32 qb + l32][16 ks + 8 hi .. +7] (zeros past N).
+  i16x8 qf[QB][D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    if (qrow < N)
-      qf[ks] = *(const i16x8*)(qh + (int64_t)qrow * D + ks * 16 + 8 * hi);
-    else
-      qf[ks] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      qf[qb][ks] = buffer_load16(rq, (uint32_t)(((wq0 + 32 * qb + l32) * D + ks * 16 + 8 * hi) * 2));
 
-  f32x16 acc_o[D / 32];
+  f32x16 acc_o[QB][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
-  // Softmax state of this lane's query. The weights of every tile are taken
-  // relative to ref = fl(c * m), the product rounded once, and ref itself is kept:
-  // alpha = 2^(ref_old - ref_new) is then exactly 1 whenever the maximum did not
-  // change. Using the exact c*m_old against the rounded c*m_new instead would
-  // scale l and U by 2^(rounding error) on every tile and drift LSE over long rows.
-  float m_run = -INFINITY;    // running raw-score maximum
-  float ref_run = -INFINITY;  // fl(c * m_run)
-  float l_run = 0.f;          // this lane's share of the exponential sum
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[qb][db][r] = 0.f;
+  // Softmax state of each of this lane's queries: the exponent reference
+  // ref = fl(c m_ref) (kept as the rounded product itself, so that
+  // alpha = 2^(ref_old - ref_new) is exactly 1 for a row whose reference did not
+  // move) and this lane's share of l.
+  float ref[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { ref[qb] = -INFINITY; l_run[qb] = 0.f; }
 
+  // Tiles [0, n_full) need no mask for any query of this workgroup; the rest
+  // (the causal diagonal band and the ragged last tile) do.
   const int n_end = CAUSAL ? min(N, m0 + BM) : N;
   const int ntiles = (n_end + BN - 1) / BN;
+  int n_full = (CAUSAL ? min(N, m0 + 1) : N) / BN;   // keys < n_full*BN are valid for every query
+  if (n_full > ntiles) n_full = ntiles;
 
+  // Global -> registers -> LDS, one tile ahead. Rows past N read as zeros (buffer
+  // bounds), so V's padding rows are finite and K's are masked.
   i16x8 kreg[PER_T], vreg[PER_T];
   auto gload = [&](int n0) {
 #pragma unroll
     for (int i = 0; i < PER_T; ++i) {
       const int ch = tid + i * NT;
       const int row = ch / CPR, col = (ch % CPR) * 8;
-      if (n0 + row < N) {
-        kreg[i] = *(const i16x8*)(kh + (int64_t)(n0 + row) * D + col);
-        vreg[i] = *(const i16x8*)(vh + (int64_t)(n0 + row) * D + col);
-      } else {
-        // keys past N: K is masked anyway, V must be finite zeros (0 * garbage may be NaN)
-        kreg[i] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        vreg[i] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+      const uint32_t off = (uint32_t)(((n0 + row) * D + col) * 2);
+      kreg[i] = buffer_load16(rk, off);
+      vreg[i] = buffer_load16(rv, off);
     }
   };
   auto lstore = [&]() {
@@ -191,91 +202,104 @@ __global__ __launch_bounds__(BM * 2) void fa_fwd_kernel(Params p) {
     }
   };
 
-  if (ntiles > 0) gload(0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int n0 = t * BN;
-    __syncthreads();                 // everyone is done reading the previous tile
-    lstore();
-    if (t + 1 < ntiles) gload(n0 + BN);  // next tile's loads overlap this tile's math
-    __syncthreads();
-    if (CAUSAL && n0 > wq0 + 31) continue;   // whole tile in this wave's future
+  // Lane (group of 16 = g, index i) of a ds_read_b64_tr_b16 receives element j
+  // from lane 4j + i/4 of its group, component i%4. With lane L of the group
+  // pointing at V[key0 + L/4][dcol0 + 4 (L%4)], lane i gets V[key0 + j][dcol0 + i],
+  // j = 0..3: four consecutive keys of one d column.
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    // ---- S^T = K_tile Q^T ----
-    f32x16 s[BN / 32];
+  auto tile = [&](int n0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // ---- S^T = K_tile Q^T: each K fragment feeds QB MFMAs ----
+    f32x16 s[QB][BN / 32];
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const i16x8 a = *(const i16x8*)(lds_k + (kb * 32 + l32) * KP + ks * 16 + 8 * hi);
-        s[kb] = mfma_32x32x16<BF16>(a, qf[ks], s[kb]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_32x32x16<BF16>(a, qf[qb][ks], s[qb][kb]);
       }
     }
-    // s[kb][r] is the raw score of query qrow and key n0 + kb*32 + 8(r/4) + 4 hi + r%4.
+    // s[qb][kb][r]: raw score of query wq0 + 32 qb + l32, key n0 + 32 kb + 8(r/4) + 4 hi + r%4.
+    if constexpr (MASK) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int query = wq0 + 32 * qb + l32;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key >= N || (CAUSAL && key > query)) s[qb][kb][r] = -INFINITY;
+          }
+      }
+    }
 
-    // ---- masks: causal diagonal and ragged tail ----
-    const bool need_mask = (n0 + BN > N) || (CAUSAL && n0 + BN - 1 > wq0);
-    if (need_mask) {
+    // ---- online softmax ----
+    bool move[QB];
+    float cand[QB];
+    bool any_move = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+      mx = max_halves(mx);
+      cand[qb] = mx * c;                     // fl(c * tile max), -inf if nothing valid
+      move[qb] = cand[qb] > ref[qb] + kTau;  // new reference needed for this query
+      any_move |= move[qb];
+    }
+    if (__builtin_amdgcn_ballot_w64(any_move)) {   // wave-uniform: rare after the first tile
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float ref_new = move[qb] ? cand[qb] : ref[qb];
+        const float alpha = __builtin_amdgcn_exp2f(ref[qb] - ref_new);   // 1 exactly if unmoved, 0 from -inf
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[qb][db][r] *= alpha;
+        ref[qb] = ref_new;
+      }
+    }
+    i16x8 pf[QB][BN / 16];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      // -inf guard: while a row has seen no valid key, use 0 as the exponent base
+      const float neg_base = (ref[qb] == -INFINITY) ? 0.f : -ref[qb];
+      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c, neg_base));
+          s[qb][kb][r] = e;
+          rs += e;
         }
-    }
-
-    // ---- online softmax ----
-    float mx = -INFINITY;
+      l_run[qb] += rs;
+      // P^T as 16-bit B operands: step tt covers s[qb][tt/2][8 (tt%2) .. +7]
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = max_halves(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float ref_new = m_new * c;
-    // -inf guard: while a row has seen no valid key, use 0 as the exponent base
-    const float base = (m_new == -INFINITY) ? 0.f : ref_new;
-    const float neg_cm = -base;
-    const float alpha = __builtin_amdgcn_exp2f(ref_run - base);
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, neg_cm));
-        s[kb][r] = e;
-        rs += e;
+      for (int tt = 0; tt < BN / 16; ++tt) {
+        const int kb = tt >> 1, base = 8 * (tt & 1);
+        e16x2 h0 = __builtin_convertvector((f32x2){s[qb][kb][base + 0], s[qb][kb][base + 1]}, e16x2);
+        e16x2 h1 = __builtin_convertvector((f32x2){s[qb][kb][base + 2], s[qb][kb][base + 3]}, e16x2);
+        e16x2 h2 = __builtin_convertvector((f32x2){s[qb][kb][base + 4], s[qb][kb][base + 5]}, e16x2);
+        e16x2 h3 = __builtin_convertvector((f32x2){s[qb][kb][base + 6], s[qb][kb][base + 7]}, e16x2);
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        pf[qb][tt] = __builtin_bit_cast(i16x8, ((u32x4){__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                                                         __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)}));
       }
-    l_run = __builtin_fmaf(l_run, alpha, rs);
-    m_run = m_new;
-    ref_run = ref_new;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-
-    // ---- P^T as 16-bit B operands: step tt covers s[tt/2][8 (tt%2) .. +7] ----
-    i16x8 pf[BN / 16];
-#pragma unroll
-    for (int tt = 0; tt < BN / 16; ++tt) {
-      const int kb = tt >> 1, base = 8 * (tt & 1);
-      uint32_t w0 = pack2<BF16>(s[kb][base + 0], s[kb][base + 1]);
-      uint32_t w1 = pack2<BF16>(s[kb][base + 2], s[kb][base + 3]);
-      uint32_t w2 = pack2<BF16>(s[kb][base + 4], s[kb][base + 5]);
-      uint32_t w3 = pack2<BF16>(s[kb][base + 6], s[kb][base + 7]);
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      pf[tt] = __builtin_bit_cast(i16x8, (u32x4){w0, w1, w2, w3});
     }
 
-    // ---- O^T += V^T P^T ----
-    // Lane (group of 16 = g, index i) of a ds_read_b64_tr_b16 receives
-    // element j from the lane 4j + i/4 of its group, component i%4. With lane L of
-    // the group pointing at V[key0 + L/4][dcol0 + 4 (L%4)], lane i gets
-    // V[key0 + j][dcol0 + i], j = 0..3: four consecutive keys of one d column.
-    const int tr_row = 4 * hi + ((lane & 15) >> 2);
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // ---- O^T += V^T P^T: each V^T fragment feeds QB MFMAs ----
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -285,30 +309,54 @@ __global__ __launch_bounds__(BM * 2) void fa_fwd_kernel(Params p) {
         const i16x4 a0 = ds_read_tr16(src);
         const i16x4 a1 = ds_read_tr16(src + 8 * VP);
         const i16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc_o[db] = mfma_32x32x16<BF16>(a, pf[tt], acc_o[db]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc_o[qb][db] = mfma_32x32x16<BF16>(a, pf[qb][tt], acc_o[qb][db]);
       }
     }
+  };
+
+  if (ntiles > 0) gload(0);
+  for (int t = 0; t < n_full; ++t) {
+    const int n0 = t * BN;
+    __syncthreads();                 // everyone is done reading the previous tile
+    lstore();
+    if (t + 1 < ntiles) gload(n0 + BN);  // next tile's loads overlap this tile's math
+    __syncthreads();
+    tile(n0, std::false_type{});
+  }
+  for (int t = n_full; t < ntiles; ++t) {
+    const int n0 = t * BN;
+    __syncthreads();
+    lstore();
+    if (t + 1 < ntiles) gload(n0 + BN);
+    __syncthreads();
+    if (CAUSAL && n0 > wq0 + 32 * QB - 1) continue;   // whole tile in this wave's future
+    tile(n0, std::true_type{});
   }
 
-  // ---- epilogue: O = U / l, LSE = ln2 (ref + log2 l) with ref = fl(c m) ----
-  const float l_tot = sum_halves(l_run);
-  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  if (qrow < N) {
-    short* orow = p.o + head + (int64_t)qrow * D;
+  // ---- epilogue: O = U / l, LSE = ln2 (ref + log2 l) ----
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = wq0 + 32 * qb + l32;
+    const float l_tot = sum_halves(l_run[qb]);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if (qrow < N) {
+      short* orow = p.o + head + (int64_t)qrow * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // acc_o[db][4g + e] holds O^T[d = 32 db + 8 g + 4 hi + e][qrow]
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        u32x2 pk;
-        pk[0] = pack2<BF16>(acc_o[db][4 * g + 0] * inv, acc_o[db][4 * g + 1] * inv);
-        pk[1] = pack2<BF16>(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv);
-        *(u32x2*)(orow + db * 32 + 8 * g + 4 * hi) = pk;
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // acc_o[qb][db][4g + e] holds O^T[d = 32 db + 8 g + 4 hi + e][qrow]
+          e16x2 lo = __builtin_convertvector((f32x2){acc_o[qb][db][4 * g + 0] * inv, acc_o[qb][db][4 * g + 1] * inv}, e16x2);
+          e16x2 up = __builtin_convertvector((f32x2){acc_o[qb][db][4 * g + 2] * inv, acc_o[qb][db][4 * g + 3] * inv}, e16x2);
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          *(u32x2*)(orow + db * 32 + 8 * g + 4 * hi) =
+              (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, up)};
+        }
+      if (hi == 0) {
+        const float lse = (l_tot > 0.f) ? kLn2 * (ref[qb] + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
+        p.lse[(int64_t)bh * N + qrow] = lse;
       }
-    if (hi == 0) {
-      const float lse = (l_tot > 0.f) ? kLn2 * (ref_run + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
-      p.lse[(int64_t)bh * N + qrow] = lse;
     }
   }
 }
@@ -317,19 +365,22 @@ __global__ __launch_bounds__(BM * 2) void fa_fwd_kernel(Params p) {
 // Host side
 // ------------------------------------------------------------------------------------
 
-struct TileShape { int bm, bn; };
-constexpr TileShape kTiles[] = {{64, 64}, {128, 64}};
+// Compiled tile shapes: block_m query rows per workgroup (NW waves x QB blocks of
+// 32 queries per wave) and block_n keys per K/V tile.
+struct TileShape { int bm, bn, nw, qb; };
+constexpr TileShape kTiles[] = {{64, 64, 2, 1}, {128, 64, 4, 1}, {256, 64, 4, 2}};
 
-template <int D, bool BF16, bool CAUSAL, int BM, int BN>
+template <int D, bool BF16, bool CAUSAL, int NW, int QB, int BN>
 hipError_t launch_one(const Params& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, BM, BN>), dim3(p.total_wgs), dim3(BM * 2), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, NW, QB, BN>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_tile(const Params& p, int bm, int bn, hipStream_t stream) {
-  if (bm == 64 && bn == 64) return launch_one<D, BF16, CAUSAL, 64, 64>(p, stream);
-  if (bm == 128 && bn == 64) return launch_one<D, BF16, CAUSAL, 128, 64>(p, stream);
+  if (bm == 64 && bn == 64) return launch_one<D, BF16, CAUSAL, 2, 1, 64>(p, stream);
+  if (bm == 128 && bn == 64) return launch_one<D, BF16, CAUSAL, 4, 1, 64>(p, stream);
+  if (bm == 256 && bn == 64) return launch_one<D, BF16, CAUSAL, 4, 2, 64>(p, stream);
   return hipErrorInvalidValue;
 }
 
@@ -356,7 +407,8 @@ fa_status validate(const void* q, const void* k, const void* v, void* o, float* 
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_MISALIGNED;
   if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
-  if (N >= ((int64_t)1 << 31) / d) return FA_ERR_TOO_LARGE;   // N*d must fit int32 offsets
+  // N*d < 2^31 elements: per-head byte offsets (and buffer ranges) fit 32 bits
+  if (N >= ((int64_t)1 << 31) / d) return FA_ERR_TOO_LARGE;
   return FA_OK;
 }
 
@@ -388,8 +440,12 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-void default_tile(int64_t N, int* bm, int* bn) {
-  *bm = (N <= 128) ? 64 : 128;
+void default_tile(int64_t N, int64_t d, int* bm, int* bn) {
+  // d = 64: two 32-query blocks per wave halve the LDS reads per MFMA and fit two
+  // waves per SIMD; d = 128 keeps one block per wave (its accumulators are twice as
+  // large). Short sequences use the smallest tile so that more workgroups exist.
+  if (N <= 128) *bm = 64;
+  else *bm = (d == 64) ? 256 : 128;
   *bn = 64;
 }
 
@@ -401,7 +457,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int64_t H, int64_t N, int64_t d, float scale, int causal, fa_dtype dtype,
                  void* stream) {
   int bm, bn;
-  default_tile(N, &bm, &bn);
+  default_tile(N, d, &bm, &bn);
   return run(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream, bm, bn);
 }
 
@@ -418,7 +474,7 @@ fa_status fa_default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal
   (void)B; (void)H; (void)causal;
   if (!block_m || !block_n) return FA_ERR_NULL_PTR;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
-  default_tile(N, block_m, block_n);
+  default_tile(N, d, block_m, block_n);
   return FA_OK;
 }
 

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 TOL_O = {"f16": 2e-3, "bf16": 1e-2}
 TOL_LSE = 1e-3
 TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
-TILES = [(64, 64), (128, 64)]
+TILES = [(64, 64), (128, 64), (256, 64)]
 
 
 def _say(msg):
@@ -77,7 +77,7 @@ def check_against_oracle(q, k, v, scale, causal, dtype, tile=None, rows=None, la
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("tile", [None, (64, 64), (128, 64)])
+@pytest.mark.parametrize("tile", [None, (64, 64), (128, 64), (256, 64)])
 def test_worked_example(dtype, causal, tile):
     g = load_worked_example()
     d = 64
