@@ -35,7 +35,36 @@ def parse():
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--traffic", type=str, default=None,
                     help="JSON file with measured per-launch HBM bytes {workload: bytes}")
+    ap.add_argument("--profile", action="store_true",
+                    help="counter-collection mode: a few launches of --workload, then a plain "
+                         "device copy of COPY_BYTES (read and written once) to calibrate the "
+                         "HBM byte counters; prints one JSON line")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30   # 1 GiB read + 1 GiB written by the calibration copy
+
+
+def profile_mode(w, launches=3):
+    import torch
+    import exact_attention_forward_fwd_amd as fa
+    from exact_attention_forward_fwd_amd.workloads import make_inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v, _ = make_inputs(w)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    tile = w.tile or (None, None)
+    for _ in range(launches):
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, block_m=tile[0], block_n=tile[1], out=o, lse=lse)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(launches):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": w.name, "launches": launches, "copy_bytes": COPY_BYTES}), flush=True)
 
 
 def time_workload(w, steps, warmup):
@@ -122,6 +151,9 @@ def main():
 
     fa.load_library()
     w = WORKLOADS[args.workload]
+    if args.profile:
+        profile_mode(w)
+        return
     r = time_workload(w, args.steps, args.warmup)
     tflops = w.flops / (r["ms_per_step"] * 1e-3) / 1e12
     achieved = w.flops / (r["kernel_ms_avg"] * 1e-3) / 1e12

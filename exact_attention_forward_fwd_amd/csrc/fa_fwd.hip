@@ -1,21 +1,23 @@
 // Exact attention forward (FlashAttention-2 loop order) for MI355X / gfx950 (CDNA4).
 //
-// One workgroup owns BM query rows of one (batch, head) slice; each of its BM/32
-// waves owns 32 of them. The workgroup streams K and V in tiles of BN keys
-// through LDS. Per tile, every wave
+// One workgroup owns BM query rows of one (batch, head) slice; each of its waves owns
+// 32 or 64 of them (one or two 32-query blocks). The workgroup streams K and V in
+// tiles of BN keys, straight from memory into double-buffered LDS. Per tile, every wave
 //   1. computes S^T = K_tile Q_w^T on v_mfma_f32_32x32x16_{f16,bf16} (fp32 acc):
 //      with the keys as MFMA rows and the queries as columns, each lane ends up
 //      holding one query's scores for 16 keys of every 32-key block, so the
-//      row (per-query) reductions are 15 in-lane ops plus one permlane32 swap;
+//      row (per-query) reductions are in-lane ops plus one permlane32 swap;
 //   2. masks the causal diagonal / ragged tail to -inf (only on tiles that need it);
-//   3. updates the online-softmax state in registers: m' = max(m, rowmax), the
-//      weights P = 2^(c x - c m') with c = s log2(e) folded into one FMA,
-//      alpha = 2^(c m - c m'), l' = alpha l + rowsum P, U' = alpha U;
+//   3. updates the online-softmax state in registers: the row maximum moves the
+//      exponent reference ref = fl(c m) only when it grows past ref + 8 (log2 units),
+//      rescaling l and U by alpha = 2^(ref_old - ref_new) then; the weights are
+//      P = 2^(c x - ref) with c = s log2(e) folded into one FMA, l' = l + rowsum P;
 //   4. rounds P to 16 bits in registers; those registers are directly the B
 //      operand of O^T += V^T P^T (the key order inside each 16-key MFMA step is
-//      permuted identically on both operands, which a sum over keys allows);
+//      permuted identically on both operands, which a sum over keys allows), issued
+//      one tile later so that these MFMAs overlap the next tile's softmax;
 //   5. reads V^T fragments with ds_read_b64_tr_b16 (transposing 16-bit LDS reads).
-// After the last tile: O = U / l, LSE = ln2 (fl(c m) + log2 l), written once.
+// After the last tile: O = U / l, LSE = ln2 (ref + log2 l), written once.
 //
 // The method is that of "用 CuTe 读懂 FlashAttention" (blog.qingsen.net): one block
 // pins a Q tile and walks the K/V tiles (its opening example and step 1), the
@@ -23,8 +25,8 @@
 // GEMM's operand (step 5), whole-tile skipping plus element masking for causal
 // (causal section) and the single final normalisation with the LSE side output
 // (final section); loop order and the -inf guard follow "CUDA 算子工程" ch. 14
-// §14.5. Register/LDS layout, the transposed-Q formulation and the instruction
-// choices are this file's own, made for CDNA4's 64-wide waves and MFMA shapes.
+// §14.5. Register/LDS layout, the transposed-Q formulation, the deferred P V and the
+// instruction choices are this file's own, made for CDNA4's 64-wide waves and MFMA shapes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
@@ -92,6 +94,10 @@ struct Params {
 // final O = U / l and LSE = ln2 (ref + log2 l) hold for any common reference.
 constexpr float kTau = 8.0f;
 
+// The P V MFMAs are issued at raised wave priority: the SIMD's other wave then gets
+// the VALU for its softmax while these MFMAs stream (measured: 5-20% faster).
+constexpr bool kRaisePvPriority = true;
+
 // Buffer resource over [base, base + bytes): loads at offsets past the end return
 // zeros, which pads the ragged last key/query tile without any branch.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -100,29 +106,61 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ i16x8 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
+// 16 bytes per lane straight from memory into LDS: lane l writes LDS bytes
+// [lds + 16 l, lds + 16 l + 16) (lds is wave-uniform); out-of-range lanes write zeros.
+__device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, short* lds, uint32_t voff,
+                                                     uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) short*)lds), 16, voff, soff,
+      0, 0);
+}
+
+// K and V tiles sit in LDS without padding, as rows of D 16-bit elements whose
+// 16-byte chunks are XOR-permuted per row: chunk c of row r is stored at chunk
+// position c ^ swz(r). For both the 32-row K fragment reads (16 lanes x 16 B) and the
+// transposing V reads (4 rows x 64 B per half wave) every access of a wave then
+// touches distinct banks. swz has period 16 in r.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
+// Two waves per SIMD: one wave's MFMAs run while the other does its softmax. The
+// register budget (<= 256 per lane) is part of the kernel's design, not a hint.
+constexpr int WAVES_PER_SIMD = 2;
 
 // NW waves per workgroup; each wave owns QB blocks of 32 queries (BM = 32 NW QB
 // query rows per workgroup) and shares every K and V fragment it reads from LDS
 // across those QB blocks.
+//
+// Pipeline (one barrier per key tile j):
+//   wait for this wave's loads, barrier      K(j) and V(j-1) are in LDS
+//   start loads K(j+1) -> kbuf[(j+1)%2], V(j) -> vbuf[j%2]   (LDS direct, async)
+//   S = K(j) Q^T                              MFMA
+//   U += V(j-1)^T P(j-1)^T                     MFMA, independent of S
+//   softmax of S -> P(j), kept for the next iteration     VALU, overlaps the PV MFMAs
+// The weights of tile j enter U one iteration later; a reference move (rare) first
+// lets the pending P(j-1) V(j-1) land in U, then scales U and l by alpha.
 template <int D, bool BF16, bool CAUSAL, int NW, int QB, int BN>
-__global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD))) void fa_fwd_kernel(Params p) {
   // Every fused multiply-add below is written out; the compiler must not fuse the
   // rounded reference products into neighbouring adds (see the softmax state note).
 #pragma clang fp contract(off)
-  constexpr int BM = 32 * NW * QB;     // query rows per workgroup
-  constexpr int NT = NW * 64;          // threads per workgroup
-  constexpr int KP = D + 8;            // K tile LDS row pitch (elements): rows shift by 16 B
-  constexpr int VP = D + 32;           // V tile LDS row pitch (elements): rows shift by 64 B
-  constexpr int CPR = D / 8;           // 16-byte chunks per row
-  constexpr int PER_T = BN * CPR / NT; // chunks of each of K and V loaded per thread per tile
-  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert((BN * CPR) % NT == 0, "loader must divide evenly");
+  constexpr int BM = 32 * NW * QB;          // query rows per workgroup
+  constexpr int TILE = BN * D;              // elements per K or V tile
+  constexpr int DMA_PER_TILE = TILE * 2 / 1024;   // 1 KB direct-to-LDS loads per tensor per tile
+  constexpr int DMA_PER_WAVE = DMA_PER_TILE / NW;
+  constexpr int ROWS_PER_DMA = 1024 / (2 * D);    // tile rows one 1 KB load covers
+  static_assert(BN % 32 == 0 && (D == 64 || D == 128), "tile shape");
+  constexpr int PATS = 16 / ROWS_PER_DMA;          // loads per 16-row swizzle period
+  static_assert(DMA_PER_TILE % NW == 0, "every wave issues the same number of loads");
   using f32x2 = float __attribute__((ext_vector_type(2)));
   using e16x2 = typename std::conditional<BF16, __bf16 __attribute__((ext_vector_type(2))),
                                           _Float16 __attribute__((ext_vector_type(2)))>::type;
 
-  __shared__ __attribute__((aligned(16))) short lds_k[BN * KP];
-  __shared__ __attribute__((aligned(16))) short lds_v[BN * VP];
+  __shared__ __attribute__((aligned(1024))) short lds_k[2][TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_v[2][TILE];
 
   // Workgroups are dispatched to the 8 XCDs round-robin (blockIdx % 8). Give each
   // XCD a contiguous range of work items so that the query blocks of one head
@@ -143,12 +181,54 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head, head_bytes);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform across the wave; saying so keeps LDS-load bases and
+  // buffer offsets in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int wq0 = m0 + wave * 32 * QB;     // first query of this wave
   const float c = p.c;
 
-  // Q^T as the B operand, kept in registers for the whole loop:
+  // ---- per-lane LDS offsets (elements), fixed for the whole loop ----
+  // K fragment (A operand of S^T = K Q^T): row 32 kb + l32, 16-byte chunk 2 ks + hi.
+  int koff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * D + (((2 * ks + hi) ^ swz<D>(l32)) << 3);
+  // V^T fragment via ds_read_b64_tr_b16. Lane (group of 16 = g, index i) receives
+  // element j from lane 4j + i/4 of its group, component i%4. With lane L of the
+  // group pointing at V[key0 + L/4][dcol0 + 4 (L%4)], lane i gets V[key0 + j][dcol0 + i],
+  // j = 0..3: four consecutive keys of one d column. Second read: keys key0 + 8...
+  int voff[D / 32][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int r = 4 * hi + ((lane & 15) >> 2) + 8 * sec;          // row within a 16-row period
+      const int ch = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+      voff[db][sec] = r * D + ((ch ^ swz<D>(r)) << 3) + 4 * (lane & 1);
+    }
+  // Direct-to-LDS loads: load i of a tile fills LDS bytes [1024 i, 1024 i + 1024),
+  // i.e. rows ROWS_PER_DMA*i.. of the tile; lane l fills tile row
+  // ROWS_PER_DMA*i + 16 l / (2D), chunk position p = (16 l mod 2D) / 16, and so fetches
+  // source chunk p ^ swz(row). This wave issues loads i = NW kk + wave.
+  uint32_t dma_off[DMA_PER_WAVE];
+#pragma unroll
+  for (int kk = 0; kk < DMA_PER_WAVE; ++kk) {
+    const int i = kk * NW + wave;
+    const int r_local = (16 * lane) / (2 * D);
+    const int pch = ((16 * lane) % (2 * D)) / 16;
+    const int r = ROWS_PER_DMA * (i % PATS) + r_local;               // tile row mod 16
+    dma_off[kk] = (uint32_t)((r_local * D + ((pch ^ swz<D>(r)) << 3)) * 2);
+  }
+  auto issue_tile_load = [&](const __amdgpu_buffer_rsrc_t& rsrc, short* dst, int n0) {
+#pragma unroll
+    for (int kk = 0; kk < DMA_PER_WAVE; ++kk) {
+      const int i = kk * NW + wave;
+      buffer_load16_to_lds(rsrc, dst + 512 * i, dma_off[kk], (uint32_t)((n0 * D + 512 * i) * 2));
+    }
+  };
+
+  // ---- Q^T as the B operand, kept in registers for the whole loop ----
   // qf[qb][ks] = Q[wq0 + 32 qb + l32][16 ks + 8 hi .. +7] (zeros past N).
   i16x8 qf[QB][D / 16];
 #pragma unroll
@@ -171,6 +251,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   float ref[QB], l_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { ref[qb] = -INFINITY; l_run[qb] = 0.f; }
+  i16x8 pprev[QB][BN / 16];   // P of the previous tile as 16-bit B operands
 
   // Tiles [0, n_full) need no mask for any query of this workgroup; the rest
   // (the causal diagonal band and the ragged last tile) do.
@@ -179,38 +260,26 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
   int n_full = (CAUSAL ? min(N, m0 + 1) : N) / BN;   // keys < n_full*BN are valid for every query
   if (n_full > ntiles) n_full = ntiles;
 
-  // Global -> registers -> LDS, one tile ahead. Rows past N read as zeros (buffer
-  // bounds), so V's padding rows are finite and K's are masked.
-  i16x8 kreg[PER_T], vreg[PER_T];
-  auto gload = [&](int n0) {
+  auto pv = [&](const short* vbuf) {
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int ch = tid + i * NT;
-      const int row = ch / CPR, col = (ch % CPR) * 8;
-      const uint32_t off = (uint32_t)(((n0 + row) * D + col) * 2);
-      kreg[i] = buffer_load16(rk, off);
-      vreg[i] = buffer_load16(rv, off);
-    }
-  };
-  auto lstore = [&]() {
+    for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-    for (int i = 0; i < PER_T; ++i) {
-      const int ch = tid + i * NT;
-      const int row = ch / CPR, col = (ch % CPR) * 8;
-      *(i16x8*)(lds_k + row * KP + col) = kreg[i];
-      *(i16x8*)(lds_v + row * VP + col) = vreg[i];
+      for (int tt = 0; tt < BN / 16; ++tt) {
+        const short* src = vbuf + ((tt >> 1) * 32 + 16 * (tt & 1)) * D;
+        const i16x4 a0 = ds_read_tr16(src + voff[db][0]);
+        const i16x4 a1 = ds_read_tr16(src + voff[db][1]);
+        const i16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc_o[qb][db] = mfma_32x32x16<BF16>(a, pprev[qb][tt], acc_o[qb][db]);
+      }
     }
   };
 
-  // Lane (group of 16 = g, index i) of a ds_read_b64_tr_b16 receives element j
-  // from lane 4j + i/4 of its group, component i%4. With lane L of the group
-  // pointing at V[key0 + L/4][dcol0 + 4 (L%4)], lane i gets V[key0 + j][dcol0 + i],
-  // j = 0..3: four consecutive keys of one d column.
-  const int tr_row = 4 * hi + ((lane & 15) >> 2);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  auto tile = [&](int n0, auto mask_tag) {
+  // One key tile: S = K(j) Q^T, then (if HAVE_PREV) the pending U += V(j-1)^T P(j-1)^T,
+  // then the softmax of S into pprev.
+  auto step = [&](int n0, const short* kbuf, const short* vprev, auto mask_tag, auto prev_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool HAVE_PREV = decltype(prev_tag)::value;
     // ---- S^T = K_tile Q^T: each K fragment feeds QB MFMAs ----
     f32x16 s[QB][BN / 32];
 #pragma unroll
@@ -221,10 +290,16 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
         for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const i16x8 a = *(const i16x8*)(lds_k + (kb * 32 + l32) * KP + ks * 16 + 8 * hi);
+        const i16x8 a = *(const i16x8*)(kbuf + kb * 32 * D + koff[ks]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_32x32x16<BF16>(a, qf[qb][ks], s[qb][kb]);
       }
+    }
+    // ---- the previous tile's P V: MFMA work that does not wait for this softmax ----
+    if constexpr (HAVE_PREV) {
+      if constexpr (kRaisePvPriority) __builtin_amdgcn_s_setprio(2);
+      pv(vprev);
+      if constexpr (kRaisePvPriority) __builtin_amdgcn_s_setprio(0);
     }
     // s[qb][kb][r]: raw score of query wq0 + 32 qb + l32, key n0 + 32 kb + 8(r/4) + 4 hi + r%4.
     if constexpr (MASK) {
@@ -257,7 +332,7 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
       move[qb] = cand[qb] > ref[qb] + kTau;  // new reference needed for this query
       any_move |= move[qb];
     }
-    if (__builtin_amdgcn_ballot_w64(any_move)) {   // wave-uniform: rare after the first tile
+    if (__builtin_amdgcn_ballot_w64(any_move)) {   // wave-uniform: rare after the first tiles
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float ref_new = move[qb] ? cand[qb] : ref[qb];
@@ -266,11 +341,10 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[qb][db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) acc_o[qb][db][r] *= alpha;    // after the pending P V landed
         ref[qb] = ref_new;
       }
     }
-    i16x8 pf[QB][BN / 16];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // -inf guard: while a row has seen no valid key, use 0 as the exponent base
@@ -294,45 +368,47 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
         e16x2 h2 = __builtin_convertvector((f32x2){s[qb][kb][base + 4], s[qb][kb][base + 5]}, e16x2);
         e16x2 h3 = __builtin_convertvector((f32x2){s[qb][kb][base + 6], s[qb][kb][base + 7]}, e16x2);
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        pf[qb][tt] = __builtin_bit_cast(i16x8, ((u32x4){__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
-                                                         __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)}));
-      }
-    }
-
-    // ---- O^T += V^T P^T: each V^T fragment feeds QB MFMAs ----
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int tt = 0; tt < BN / 16; ++tt) {
-        const int key0 = (tt >> 1) * 32 + 16 * (tt & 1) + tr_row;
-        const short* src = lds_v + key0 * VP + db * 32 + tr_col;
-        const i16x4 a0 = ds_read_tr16(src);
-        const i16x4 a1 = ds_read_tr16(src + 8 * VP);
-        const i16x8 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc_o[qb][db] = mfma_32x32x16<BF16>(a, pf[qb][tt], acc_o[qb][db]);
+        pprev[qb][tt] = __builtin_bit_cast(i16x8, ((u32x4){__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                                                            __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)}));
       }
     }
   };
 
-  if (ntiles > 0) gload(0);
-  for (int t = 0; t < n_full; ++t) {
-    const int n0 = t * BN;
-    __syncthreads();                 // everyone is done reading the previous tile
-    lstore();
-    if (t + 1 < ntiles) gload(n0 + BN);  // next tile's loads overlap this tile's math
+  // LDS stores by other waves' direct loads become visible after this wave's own
+  // loads have landed (vmcnt) and everyone has passed the barrier.
+  auto sync_tile = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads are in LDS
     __syncthreads();
-    tile(n0, std::false_type{});
+  };
+
+  bool have_prev = false;   // pprev holds the weights of tile j-1 (wave-uniform)
+  if (ntiles > 0) issue_tile_load(rk, lds_k[0], 0);
+  int j = 0;
+  for (; j < n_full; ++j) {
+    const int n0 = j * BN;
+    sync_tile();
+    if (j + 1 < ntiles) issue_tile_load(rk, lds_k[(j + 1) & 1], n0 + BN);
+    issue_tile_load(rv, lds_v[j & 1], n0);
+    if (j == 0) step(n0, lds_k[0], lds_v[1], std::false_type{}, std::false_type{});
+    else step(n0, lds_k[j & 1], lds_v[(j - 1) & 1], std::false_type{}, std::true_type{});
+    have_prev = true;
   }
-  for (int t = n_full; t < ntiles; ++t) {
-    const int n0 = t * BN;
-    __syncthreads();
-    lstore();
-    if (t + 1 < ntiles) gload(n0 + BN);
-    __syncthreads();
-    if (CAUSAL && n0 > wq0 + 32 * QB - 1) continue;   // whole tile in this wave's future
-    tile(n0, std::true_type{});
+  for (; j < ntiles; ++j) {
+    const int n0 = j * BN;
+    sync_tile();
+    if (j + 1 < ntiles) issue_tile_load(rk, lds_k[(j + 1) & 1], n0 + BN);
+    issue_tile_load(rv, lds_v[j & 1], n0);
+    if (CAUSAL && n0 > wq0 + 32 * QB - 1) {   // whole tile in this wave's future
+      if (have_prev) pv(lds_v[(j - 1) & 1]);
+      have_prev = false;
+      continue;
+    }
+    if (have_prev) step(n0, lds_k[j & 1], lds_v[(j - 1) & 1], std::true_type{}, std::true_type{});
+    else step(n0, lds_k[j & 1], lds_v[(j - 1) & 1], std::true_type{}, std::false_type{});
+    have_prev = true;
   }
+  sync_tile();                                  // V of the last tile is in LDS
+  if (have_prev) pv(lds_v[(ntiles - 1) & 1]);
 
   // ---- epilogue: O = U / l, LSE = ln2 (ref + log2 l) ----
 #pragma unroll
@@ -368,7 +444,8 @@ __global__ __launch_bounds__(NW * 64) void fa_fwd_kernel(Params p) {
 // Compiled tile shapes: block_m query rows per workgroup (NW waves x QB blocks of
 // 32 queries per wave) and block_n keys per K/V tile.
 struct TileShape { int bm, bn, nw, qb; };
-constexpr TileShape kTiles[] = {{64, 64, 2, 1}, {128, 64, 4, 1}, {256, 64, 4, 2}};
+constexpr TileShape kTiles[] = {{64, 64, 2, 1}, {128, 64, 4, 1}, {256, 64, 4, 2},
+                                 {128, 32, 4, 1}, {256, 32, 4, 2}};
 
 template <int D, bool BF16, bool CAUSAL, int NW, int QB, int BN>
 hipError_t launch_one(const Params& p, hipStream_t stream) {
@@ -380,7 +457,12 @@ template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_tile(const Params& p, int bm, int bn, hipStream_t stream) {
   if (bm == 64 && bn == 64) return launch_one<D, BF16, CAUSAL, 2, 1, 64>(p, stream);
   if (bm == 128 && bn == 64) return launch_one<D, BF16, CAUSAL, 4, 1, 64>(p, stream);
-  if (bm == 256 && bn == 64) return launch_one<D, BF16, CAUSAL, 4, 2, 64>(p, stream);
+  if (bm == 128 && bn == 32) return launch_one<D, BF16, CAUSAL, 4, 1, 32>(p, stream);
+  if constexpr (D == 64) {
+    // two query blocks per wave: at d = 128 their accumulators do not fit the budget
+    if (bm == 256 && bn == 64) return launch_one<D, BF16, CAUSAL, 4, 2, 64>(p, stream);
+    if (bm == 256 && bn == 32) return launch_one<D, BF16, CAUSAL, 4, 2, 32>(p, stream);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -393,7 +475,7 @@ hipError_t launch_d(const Params& p, bool bf16, bool causal, int bm, int bn, hip
 bool tile_ok(int64_t d, int bm, int bn) {
   if (d != 64 && d != 128) return false;
   for (const TileShape& t : kTiles)
-    if (t.bm == bm && t.bn == bn) return true;
+    if (t.bm == bm && t.bn == bn) return !(d == 128 && t.qb > 1);
   return false;
 }
 
@@ -440,13 +522,23 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-void default_tile(int64_t N, int64_t d, int* bm, int* bn) {
-  // d = 64: two 32-query blocks per wave halve the LDS reads per MFMA and fit two
-  // waves per SIMD; d = 128 keeps one block per wave (its accumulators are twice as
-  // large). Short sequences use the smallest tile so that more workgroups exist.
-  if (N <= 128) *bm = 64;
-  else *bm = (d == 64) ? 256 : 128;
-  *bn = 64;
+void default_tile(int64_t N, int64_t d, int causal, int* bm, int* bn) {
+  // Measured on MI355X (one tile sweep per workload family):
+  //  - short sequences: the smallest tile, so that more workgroups exist;
+  //  - d = 64, non-causal: two 32-query blocks per wave share every K/V fragment
+  //    read (half the LDS traffic per MFMA), 32-key tiles keep it within 256 VGPRs;
+  //  - d = 128, non-causal: one block per wave, 32-key tiles (no spills);
+  //  - causal: 64-key tiles, fewer diagonal tiles and barriers per row block.
+  if (N <= 128) {
+    *bm = 64;
+    *bn = 64;
+  } else if (causal) {
+    *bm = 128;
+    *bn = 64;
+  } else {
+    *bm = (d == 64) ? 256 : 128;
+    *bn = 32;
+  }
 }
 
 }  // namespace
@@ -457,7 +549,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int64_t H, int64_t N, int64_t d, float scale, int causal, fa_dtype dtype,
                  void* stream) {
   int bm, bn;
-  default_tile(N, d, &bm, &bn);
+  default_tile(N, d, causal, &bm, &bn);
   return run(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream, bm, bn);
 }
 
@@ -471,10 +563,10 @@ int fa_tile_supported(int64_t d, int block_m, int block_n) { return tile_ok(d, b
 
 fa_status fa_default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int* block_m,
                           int* block_n) {
-  (void)B; (void)H; (void)causal;
+  (void)B; (void)H;
   if (!block_m || !block_n) return FA_ERR_NULL_PTR;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
-  default_tile(N, d, block_m, block_n);
+  default_tile(N, d, causal, block_m, block_n);
   return FA_OK;
 }
 
