@@ -33,8 +33,10 @@ def parse():
     ap.add_argument("--workload", type=int, default=HEADLINE, help="1..5 (default: the headline 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
-    ap.add_argument("--traffic", type=str, default=None,
-                    help="JSON file with measured per-launch HBM bytes {workload: bytes}")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="turn two rocprofv3 --pmc runs of --profile (FETCH_SIZE, then WRITE_SIZE; "
+                         "--output-format csv) into a calibrated per-launch HBM traffic record "
+                         "(JSON on stdout); needs no GPU")
     ap.add_argument("--profile", action="store_true",
                     help="counter-collection mode: a few launches of --workload, then a plain "
                          "device copy of COPY_BYTES (read and written once) to calibrate the "
@@ -43,6 +45,74 @@ def parse():
 
 
 COPY_BYTES = 1 << 30   # 1 GiB read + 1 GiB written by the calibration copy
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_forward_fwd_amd", "csrc", "fa_fwd.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def algorithmic_bytes(w) -> int:
+    """Compulsory HBM bytes of one launch: Q, K, V read once, O written once (all in
+    the 16-bit input type), LSE written once in fp32."""
+    elems = w.B * w.H * w.N * w.d
+    return 4 * elems * 2 + w.B * w.H * w.N * 4
+
+
+def _pmc_rows(d, counter):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    fa_vals, copy_vals = [], []
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            if "fa_fwd_kernel" in name:
+                fa_vals.append((name, float(row["Counter_Value"])))
+            elif "copyBuffer" in name:
+                copy_vals.append(float(row["Counter_Value"]))
+    if not fa_vals or not copy_vals:
+        raise SystemExit(f"{d}: missing fa_fwd_kernel or copy dispatches for {counter}")
+    return fa_vals, copy_vals
+
+
+def traffic_record(w, fetch_dir, write_dir):
+    """Per-launch HBM bytes of the attention kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) each scaled by bytes / counter of a plain device copy of COPY_BYTES."""
+    fa_f, cp_f = _pmc_rows(fetch_dir, "FETCH_SIZE")
+    fa_w, cp_w = _pmc_rows(write_dir, "WRITE_SIZE")
+    kib = lambda v: sum(v) / len(v)
+    fetch_kib, write_kib = kib([v for _, v in fa_f]), kib([v for _, v in fa_w])
+    copy_fetch_kib, copy_write_kib = kib(cp_f), kib(cp_w)
+    f_fac = COPY_BYTES / (copy_fetch_kib * 1024)
+    w_fac = COPY_BYTES / (copy_write_kib * 1024)
+    hbm = fetch_kib * 1024 * f_fac + write_kib * 1024 * w_fac
+    return {"workload": w.name, "kernel": fa_f[0][0], "kernel_source_sha256": kernel_source_hash(),
+            "fetch_kib_per_dispatch": fetch_kib, "write_kib_per_dispatch": write_kib,
+            "copy_bytes": COPY_BYTES, "copy_fetch_kib": copy_fetch_kib, "copy_write_kib": copy_write_kib,
+            "fetch_factor": f_fac, "write_factor": w_fac, "hbm_bytes_per_launch": hbm,
+            "algorithmic_bytes_per_launch": algorithmic_bytes(w),
+            "traffic_over_algorithmic": hbm / algorithmic_bytes(w)}
+
+
+def stored_traffic(w):
+    """The committed traffic record for this workload, if it was taken on the current
+    kernel source; else None."""
+    path = os.path.join(PROFILES, f"traffic_{w.name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec
 
 
 def profile_mode(w, launches=3):
@@ -138,6 +208,10 @@ def cpu_baseline(w, budget_s=12.0):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        from exact_attention_forward_fwd_amd.workloads import WORKLOADS
+        print(json.dumps(traffic_record(WORKLOADS[args.workload], *args.traffic_from), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
               "multi-GPU mode (run with --gpus 1)", file=sys.stderr)
@@ -157,9 +231,9 @@ def main():
     r = time_workload(w, args.steps, args.warmup)
     tflops = w.flops / (r["ms_per_step"] * 1e-3) / 1e12
     achieved = w.flops / (r["kernel_ms_avg"] * 1e-3) / 1e12
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        traffic = json.load(open(args.traffic)).get(str(w.index))
+    rec = stored_traffic(w)
+    traffic = round(rec["hbm_bytes_per_launch"]) if rec else None
+    alg_bytes = algorithmic_bytes(w)
     out = {
         "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, halved for causal) and % of MFMA peak",
         "value": round(tflops, 2),
@@ -180,8 +254,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic,
+                     "algorithmic_bytes": alg_bytes,
+                     "algorithmic_flop": w.flops,
                      "kernel_ms_avg": round(r["kernel_ms_avg"], 5),
-                     "kernel_ms_median": round(r["kernel_ms_median"], 5)},
+                     "kernel_ms_median": round(r["kernel_ms_median"], 5),
+                     "hbm_gbs_algorithmic": round(alg_bytes / (r["kernel_ms_avg"] * 1e-3) / 1e9, 1)},
     }
     del r
     if not args.no_others:

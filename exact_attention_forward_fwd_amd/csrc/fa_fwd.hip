@@ -159,8 +159,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   using e16x2 = typename std::conditional<BF16, __bf16 __attribute__((ext_vector_type(2))),
                                           _Float16 __attribute__((ext_vector_type(2)))>::type;
 
-  __shared__ __attribute__((aligned(1024))) short lds_k[2][TILE];
-  __shared__ __attribute__((aligned(1024))) short lds_v[2][TILE];
+  // Two stages per tensor, as four distinct LDS objects: with the tile loop unrolled
+  // by two every access names its stage at compile time, so the compiler can tell
+  // the stage being read from the one the in-flight direct loads are filling and
+  // does not wait for those loads before reading.
+  __shared__ __attribute__((aligned(1024))) short lds_k0[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_k1[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_v0[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_v1[TILE];
 
   // Workgroups are dispatched to the 8 XCDs round-robin (blockIdx % 8). Give each
   // XCD a contiguous range of work items so that the query blocks of one head
@@ -381,34 +387,51 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     __syncthreads();
   };
 
-  bool have_prev = false;   // pprev holds the weights of tile j-1 (wave-uniform)
-  if (ntiles > 0) issue_tile_load(rk, lds_k[0], 0);
-  int j = 0;
-  for (; j < n_full; ++j) {
+  // Tile j reads K(j) from stage j%2 and V(j-1) from stage (j-1)%2 while the direct
+  // loads fill K(j+1) into stage (j+1)%2 and V(j) into stage j%2.
+  auto full_tile = [&](int j, short* k_rd, short* k_wr, short* v_rd, short* v_wr, auto prev_tag) {
     const int n0 = j * BN;
     sync_tile();
-    if (j + 1 < ntiles) issue_tile_load(rk, lds_k[(j + 1) & 1], n0 + BN);
-    issue_tile_load(rv, lds_v[j & 1], n0);
-    if (j == 0) step(n0, lds_k[0], lds_v[1], std::false_type{}, std::false_type{});
-    else step(n0, lds_k[j & 1], lds_v[(j - 1) & 1], std::false_type{}, std::true_type{});
+    if (j + 1 < ntiles) issue_tile_load(rk, k_wr, n0 + BN);
+    issue_tile_load(rv, v_wr, n0);
+    step(n0, k_rd, v_rd, std::false_type{}, prev_tag);
+  };
+  bool have_prev = false;   // pprev holds the weights of tile j-1 (wave-uniform)
+  if (ntiles > 0) issue_tile_load(rk, lds_k0, 0);
+  int j = 0;
+  if (n_full > 0) {
+    full_tile(0, lds_k0, lds_k1, lds_v1, lds_v0, std::false_type{});
+    j = 1;
+    for (; j + 1 < n_full; j += 2) {
+      full_tile(j, lds_k1, lds_k0, lds_v0, lds_v1, std::true_type{});
+      full_tile(j + 1, lds_k0, lds_k1, lds_v1, lds_v0, std::true_type{});
+    }
+    if (j < n_full) {
+      full_tile(j, lds_k1, lds_k0, lds_v0, lds_v1, std::true_type{});
+      ++j;
+    }
     have_prev = true;
   }
   for (; j < ntiles; ++j) {
     const int n0 = j * BN;
+    short* k_rd = (j & 1) ? lds_k1 : lds_k0;
+    short* k_wr = (j & 1) ? lds_k0 : lds_k1;
+    short* v_rd = (j & 1) ? lds_v0 : lds_v1;
+    short* v_wr = (j & 1) ? lds_v1 : lds_v0;
     sync_tile();
-    if (j + 1 < ntiles) issue_tile_load(rk, lds_k[(j + 1) & 1], n0 + BN);
-    issue_tile_load(rv, lds_v[j & 1], n0);
+    if (j + 1 < ntiles) issue_tile_load(rk, k_wr, n0 + BN);
+    issue_tile_load(rv, v_wr, n0);
     if (CAUSAL && n0 > wq0 + 32 * QB - 1) {   // whole tile in this wave's future
-      if (have_prev) pv(lds_v[(j - 1) & 1]);
+      if (have_prev) pv(v_rd);
       have_prev = false;
       continue;
     }
-    if (have_prev) step(n0, lds_k[j & 1], lds_v[(j - 1) & 1], std::true_type{}, std::true_type{});
-    else step(n0, lds_k[j & 1], lds_v[(j - 1) & 1], std::true_type{}, std::false_type{});
+    if (have_prev) step(n0, k_rd, v_rd, std::true_type{}, std::true_type{});
+    else step(n0, k_rd, v_rd, std::true_type{}, std::false_type{});
     have_prev = true;
   }
   sync_tile();                                  // V of the last tile is in LDS
-  if (have_prev) pv(lds_v[(ntiles - 1) & 1]);
+  if (have_prev) pv(((ntiles - 1) & 1) ? lds_v1 : lds_v0);
 
   // ---- epilogue: O = U / l, LSE = ln2 (ref + log2 l) ----
 #pragma unroll
@@ -528,13 +551,14 @@ void default_tile(int64_t N, int64_t d, int causal, int* bm, int* bn) {
   //  - d = 64, non-causal: two 32-query blocks per wave share every K/V fragment
   //    read (half the LDS traffic per MFMA), 32-key tiles keep it within 256 VGPRs;
   //  - d = 128, non-causal: one block per wave, 32-key tiles (no spills);
-  //  - causal: 64-key tiles, fewer diagonal tiles and barriers per row block.
+  //  - causal: one block per wave (row blocks of uneven length balance better);
+  //    64-key tiles at d = 64, 32-key tiles at d = 128 (no spills).
   if (N <= 128) {
     *bm = 64;
     *bn = 64;
   } else if (causal) {
     *bm = 128;
-    *bn = 64;
+    *bn = (d == 64) ? 64 : 32;
   } else {
     *bm = (d == 64) ? 256 : 128;
     *bn = 32;
