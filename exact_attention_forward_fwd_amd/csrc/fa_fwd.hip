@@ -93,6 +93,17 @@ struct Params {
 // inside fp16's range) and skips the rescale of l and U on almost every tile. The
 // final O = U / l and LSE = ln2 (ref + log2 l) hold for any common reference.
 constexpr float kTau = 8.0f;
+#ifndef PP_VALU_PRIO
+#define PP_VALU_PRIO 0
+#endif
+#ifndef PP_MFMA_PRIO
+#define PP_MFMA_PRIO 0
+#endif
+constexpr int kPpValuPrio = PP_VALU_PRIO;
+constexpr int kPpMfmaPrio = PP_MFMA_PRIO;
+// The ping-pong kernel keeps its reference while a lane's weights of one tile sum to
+// at most this (so each weight is at most 2^kTau as well).
+constexpr float kSumMax = 256.0f;
 
 // The P V MFMAs are issued at raised wave priority: the SIMD's other wave then gets
 // the VALU for its softmax while these MFMAs stream (measured: 5-20% faster).
@@ -461,18 +472,406 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
 }
 
 // ------------------------------------------------------------------------------------
+// Ping-pong kernel: eight waves, two per SIMD, taking turns on the matrix pipe.
+// ------------------------------------------------------------------------------------
+//
+// A wave cannot overlap its own MFMAs with its own VALU work: measured on gfx950, one
+// wave interleaving an MFMA with 16 FMAs takes about as long as the two streams
+// back to back, while an MFMA-only wave and a VALU-only wave sharing a SIMD run at
+// nearly their standalone rates. So the workgroup has eight waves; waves w and w+4
+// share a SIMD (measured with HW_ID), and the two groups G0 = {0..3}, G1 = {4..7}
+// run the same sequence of clusters one phase apart, separated by workgroup barriers:
+//
+//   phase 2j   : G0 runs M(j)            G1 runs V(j-1)
+//   phase 2j+1 : G0 runs V(j)            G1 runs M(j)
+//
+//   M(j) = S(j) = K(j) Q^T and U += V(j-1)^T P(j-1)^T    (16 MFMAs from registers)
+//   V(j) = softmax of S(j) into P(j); LDS reads of the K(j+1) and V(j) fragments
+//          that M(j+1) consumes                          (VALU and LDS)
+//
+// so on every SIMD one wave feeds the matrix pipe while the other does its softmax.
+// K and V tiles are double-buffered in LDS. The G0 waves issue all direct loads:
+// K(j+2) and V(j+1) at the end of V(j) (phase 2j+1), after their own reads of that
+// cluster, and wait for them at the end of M(j+1) (phase 2j+2), before the barrier.
+// K(j+1) and V(j) are read in phases 2j+1 (G0) and 2j+2 (G1); their stages are
+// refilled from the end of phase 2j+3 on. Every barrier also waits for the wave's
+// LDS reads, so no stage is overwritten while a read of it is in flight. No wave
+// ever reads LDS while one of its own direct loads is pending, so the compiler
+// needs no wait between the two even though it cannot tell the stages apart.
+template <int D, bool BF16, bool CAUSAL, int QB, int BN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_pp_kernel(Params p) {
+#pragma clang fp contract(off)
+  constexpr int NWAVES = 8;
+  constexpr int BM = 32 * NWAVES * QB;        // query rows per workgroup
+  constexpr int TILE = BN * D;                // elements per K or V tile
+  constexpr int DMA_PER_TILE = TILE * 2 / 1024;
+  constexpr int LOADS_PER_WAVE = 2 * DMA_PER_TILE / (NWAVES / 2);   // G0 issues all loads
+  constexpr int ROWS_PER_DMA = 1024 / (2 * D);
+  constexpr int PATS = 16 / ROWS_PER_DMA;
+  constexpr int NKB = BN / 32, NKS = D / 16, NDB = D / 32, NTT = BN / 16;
+  constexpr int NQK = NKB * NKS * QB, NPV = NDB * NTT * QB;
+  static_assert(BN % 32 == 0 && (D == 64 || D == 128), "tile shape");
+  static_assert((2 * DMA_PER_TILE) % (NWAVES / 2) == 0, "every G0 wave issues the same number of loads");
+  static_assert(NQK == NPV, "the M cluster interleaves the two products one to one");
+  using f32x2 = float __attribute__((ext_vector_type(2)));
+  using e16x2 = typename std::conditional<BF16, __bf16 __attribute__((ext_vector_type(2))),
+                                          _Float16 __attribute__((ext_vector_type(2)))>::type;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+  __shared__ __attribute__((aligned(1024))) short lds_k0[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_k1[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_v0[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_v1[TILE];
+
+  // ---- work item (XCD-contiguous, causal heavy-first) ----
+  const int bid = blockIdx.x;
+  const int T_all = p.total_wgs;
+  const int xcd = bid & 7, slot = bid >> 3, per = T_all >> 3, rem = T_all & 7;
+  const int w = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int bh = w / p.num_m_blocks;
+  int mb = w - bh * p.num_m_blocks;
+  if (CAUSAL) mb = p.num_m_blocks - 1 - mb;
+  const int N = p.N;
+  const int m0 = mb * BM;
+  const int64_t head = (int64_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head, head_bytes);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;                  // 0: leads by one phase, 1: follows
+  const int lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  // The two waves of a SIMD (w, w+4) own adjacent row blocks, so under a causal
+  // mask they run out of work on the same tile.
+  const int wq0 = m0 + 32 * QB * (2 * (wave & 3) + grp);
+  const float c = p.c;
+
+  // tiles the workgroup streams, tiles this wave computes, tiles it needs no mask for
+  const int n_end = CAUSAL ? min(N, m0 + BM) : N;
+  const int T = (n_end + BN - 1) / BN;
+  int Tw = 0, n_full = 0;
+  if (wq0 < N) {
+    const int w_end = CAUSAL ? min(N, wq0 + 32 * QB) : N;
+    Tw = (w_end + BN - 1) / BN;
+    n_full = min(Tw, (CAUSAL ? min(N, wq0 + 1) : N) / BN);
+  }
+
+  // ---- LDS fragment offsets (elements), as in fa_fwd_kernel ----
+  int koff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = l32 * D + (((2 * ks + hi) ^ swz<D>(l32)) << 3);
+  int voff[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int r = 4 * hi + ((lane & 15) >> 2) + 8 * sec;
+      const int ch = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+      voff[db][sec] = r * D + ((ch ^ swz<D>(r)) << 3) + 4 * (lane & 1);
+    }
+
+  // ---- direct-load assignment: load i of a phase (i < DMA_PER_TILE: K chunk i,
+  // else V chunk i - DMA_PER_TILE) is issued by G0 wave i % 4 ----
+  uint32_t dma_off[LOADS_PER_WAVE];
+  int dma_chunk[LOADS_PER_WAVE];
+  bool dma_is_k[LOADS_PER_WAVE];
+#pragma unroll
+  for (int t = 0; t < LOADS_PER_WAVE; ++t) {
+    const int i = (wave & 3) + (NWAVES / 2) * t;
+    dma_is_k[t] = i < DMA_PER_TILE;
+    const int ch = dma_is_k[t] ? i : i - DMA_PER_TILE;
+    dma_chunk[t] = ch;
+    const int r_local = (16 * lane) / (2 * D);
+    const int pch = ((16 * lane) % (2 * D)) / 16;
+    const int r = ROWS_PER_DMA * (ch % PATS) + r_local;
+    dma_off[t] = (uint32_t)((r_local * D + ((pch ^ swz<D>(r)) << 3)) * 2);
+  }
+  // loads of K(jk) into kdst (if has_k) and V(jv) into vdst (if has_v); wave-uniform flags
+  auto issue_loads = [&](short* kdst, short* vdst, int jk, int jv, bool has_k, bool has_v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < LOADS_PER_WAVE; ++t) {
+      if (dma_is_k[t]) {
+        if (has_k)
+          buffer_load16_to_lds(rk, kdst + 512 * dma_chunk[t], dma_off[t], (uint32_t)((jk * BN * D + 512 * dma_chunk[t]) * 2));
+      } else {
+        if (has_v)
+          buffer_load16_to_lds(rv, vdst + 512 * dma_chunk[t], dma_off[t], (uint32_t)((jv * BN * D + 512 * dma_chunk[t]) * 2));
+      }
+    }
+  };
+  // End of a phase: wait for this wave's LDS reads (always) and direct loads (if
+  // wait_loads), then the workgroup barrier. No instruction moves across it.
+  auto phase_end = [&](bool wait_loads) __attribute__((always_inline)) {
+    if (wait_loads) __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- registers ----
+  i16x8 qf[QB][NKS];                 // Q^T, B operand of S^T = K Q^T
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[qb][ks] = buffer_load16(rq, (uint32_t)(((wq0 + 32 * qb + l32) * D + ks * 16 + 8 * hi) * 2));
+  f32x16 acc_o[QB][NDB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[qb][db][r] = 0.f;
+  float ref[QB], nb[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { ref[qb] = -INFINITY; nb[qb] = 0.f; l_run[qb] = 0.f; }
+  i16x8 kf[NKB][NKS];                // K fragments of the tile the next M cluster multiplies
+  i16x8 vf[NDB][NTT];                // V^T fragments of the tile whose P is pending
+  f32x16 s[QB][NKB];                 // scores, then weights, of the current tile
+  i16x8 pk[QB][NTT];                 // pending P as 16-bit B operands
+
+  auto read_k = [&](const short* kbuf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) kf[kb][ks] = *(const i16x8*)(kbuf + kb * 32 * D + koff[ks]);
+  };
+  auto read_v = [&](const short* vbuf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      const short* src = vbuf + ((tt >> 1) * 32 + 16 * (tt & 1)) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const i16x4 a0 = ds_read_tr16(src + voff[db][0]);
+        const i16x4 a1 = ds_read_tr16(src + voff[db][1]);
+        vf[db][tt] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+  };
+  // i-th MFMA of each product: QK steps run ks-major so that consecutive steps of one
+  // accumulator are NQK / NKS apart; PV steps run tt-major likewise.
+  auto qk_step = [&](int i) __attribute__((always_inline)) {
+    const int ks = i / (NKB * QB), kb = (i / QB) % NKB, qb = i % QB;
+    if (ks == 0) s[qb][kb] = mfma_32x32x16<BF16>(kf[kb][ks], qf[qb][ks], (f32x16){});
+    else s[qb][kb] = mfma_32x32x16<BF16>(kf[kb][ks], qf[qb][ks], s[qb][kb]);
+  };
+  auto pv_step = [&](int i) __attribute__((always_inline)) {
+    const int tt = i / (NDB * QB), db = (i / QB) % NDB, qb = i % QB;
+    acc_o[qb][db] = mfma_32x32x16<BF16>(vf[db][tt], pk[qb][tt], acc_o[qb][db]);
+  };
+  // M cluster: both products, interleaved one to one. It runs in every iteration of
+  // every wave, so that the loop has one code path: where a product is not needed
+  // its result is unused (S of a tile past this wave's rows) or zero (P is zero
+  // before the first tile and after the wave's last one).
+  auto m_cluster = [&]() __attribute__((always_inline)) {
+    if constexpr (kPpMfmaPrio != 0) __builtin_amdgcn_s_setprio(kPpMfmaPrio);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) { qk_step(i); pv_step(i); }
+    if constexpr (kPpMfmaPrio != 0) __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Softmax of tile j (keys n0..n0+BN) in s, into pk; l, ref and (rarely) U updated.
+  // The common path needs no row maximum: the weights are formed against the current
+  // reference, P = 2^(c x + nb) with nb = -ref, and their per-lane sum both updates l
+  // and checks the reference. While every lane's sum of this tile's weights is at
+  // most 2^kTau, every weight is too (and far inside fp16's range). Otherwise (a new
+  // maximum well above the reference, an infinite weight, or the first tile, whose
+  // reference is still -inf) the wave takes the rare path: each query's reference
+  // moves up to its row maximum, l and U are scaled by alpha = 2^(ref_old - ref_new),
+  // and the tile's weights are recomputed (s is still intact). After a move every
+  // weight of the tile is at most 1, so one redo suffices.
+  auto weights = [&](float (&rs)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float part[2] = {0.f, 0.f};   // two partial sums: shorter dependency chains
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        const int kb = tt >> 1, base = 8 * (tt & 1);
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + i], c, nb[qb]));
+        e16x2 h[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = __builtin_convertvector((f32x2){e[2 * i], e[2 * i + 1]}, e16x2);
+        pk[qb][tt] = __builtin_bit_cast(i16x8, ((u32x4){__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
+                                                        __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])}));
+        // l sums the fp32 weights. (A dot2 over the packed weights would issue half as
+        // many instructions, but on gfx950 it waits for the matrix pipe, which the
+        // other wave of the SIMD keeps busy: measured 24 cycles per dot2 against 6 per add.)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part[i & 1] += e[i];
+      }
+      rs[qb] = part[0] + part[1];
+    }
+  };
+  auto softmax = [&](int n0, bool mask) __attribute__((always_inline)) {
+    if (mask) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int query = wq0 + 32 * qb + l32;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key >= N || (CAUSAL && key > query)) s[qb][kb][r] = -INFINITY;
+          }
+      }
+    }
+    float rs[QB];
+    weights(rs);
+    bool redo = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) redo |= !(rs[qb] <= kSumMax) || ref[qb] == -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(redo)) {   // wave-uniform, rare after the first tile
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+        const float cand = max_halves(mx) * c;             // fl(c * row max), -inf if none valid
+        const float ref_new = cand > ref[qb] ? cand : ref[qb];
+        const float alpha = __builtin_amdgcn_exp2f(ref[qb] - ref_new);   // 1 exactly if unmoved, 0 from -inf
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[qb][db][r] *= alpha;
+        ref[qb] = ref_new;
+        nb[qb] = (ref_new == -INFINITY) ? 0.f : -ref_new;  // -inf guard: base 0 until a valid key
+      }
+      weights(rs);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+  };
+
+  // The compiler may move arithmetic across the barrier asm (it is not a memory
+  // operation); an empty asm that reads and writes a value pins its computation to
+  // the phase that produced it.
+  auto pin_softmax_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) asm volatile("" : "+v"(pk[qb][tt]));
+      asm volatile("" : "+v"(l_run[qb]), "+v"(ref[qb]), "+v"(nb[qb]));
+    }
+  };
+  // V cluster of tile j: fragment reads for the next M cluster (always issued; a
+  // stage holding no needed tile is read harmlessly), then the softmax, or P = 0
+  // for a tile this wave does not compute.
+  auto v_cluster = [&](int j, const short* k_next, const short* v_cur) __attribute__((always_inline)) {
+    if constexpr (kPpValuPrio != 0) __builtin_amdgcn_s_setprio(kPpValuPrio);
+    read_k(k_next);
+    read_v(v_cur);
+    if (j < Tw) {
+      softmax(j * BN, j >= n_full);
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) pk[qb][tt] = (i16x8){};
+    }
+    pin_softmax_state();
+    if constexpr (kPpValuPrio != 0) __builtin_amdgcn_s_setprio(0);
+  };
+
+  // ---- prologue: K(0), V(0), K(1) in LDS; K(0) fragments in registers ----
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) pk[qb][tt] = (i16x8){};
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) vf[db][tt] = (i16x8){};
+  if (grp == 0) {
+    issue_loads(lds_k0, lds_v0, 0, 0, true, true);
+    if (T > 1) issue_loads(lds_k1, lds_v1, 1, 0, true, false);
+  }
+  phase_end(true);
+  read_k(lds_k0);
+  if (grp == 1) phase_end(false);            // G1 sits out phase 0
+
+  // iteration j: M(j), barrier, V(j), barrier. Unrolled by two, so that every LDS
+  // stage is named at compile time and its offset folds into the instructions.
+  auto iteration = [&](int j, auto odd_tag) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(odd_tag)::value;
+    short* k_ld = ODD ? lds_k1 : lds_k0;          // K(j+2) -> stage j%2
+    short* v_ld = ODD ? lds_v0 : lds_v1;          // V(j+1) -> stage (j+1)%2
+    const short* k_rd = ODD ? lds_k0 : lds_k1;    // K(j+1) in stage (j+1)%2
+    const short* v_rd = ODD ? lds_v1 : lds_v0;    // V(j) in stage j%2
+    m_cluster();
+    phase_end(grp == 0);
+    v_cluster(j, k_rd, v_rd);
+    if (grp == 0) issue_loads(k_ld, v_ld, j + 2, j + 1, j + 2 < T, j + 1 < T);
+    phase_end(false);
+  };
+  int j = 0;
+  for (; j + 1 < T; j += 2) {
+    iteration(j, std::false_type{});
+    iteration(j + 1, std::true_type{});
+  }
+  if (j < T) iteration(j, std::false_type{});
+
+  // ---- final cluster: the last pending P V, then O = U / l and LSE ----
+  // (its P is zero unless this wave computed the last tile)
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) pv_step(i);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = wq0 + 32 * qb + l32;
+    const float l_tot = sum_halves(l_run[qb]);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if (qrow < N) {
+      short* orow = p.o + head + (int64_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          e16x2 lo = __builtin_convertvector((f32x2){acc_o[qb][db][4 * g + 0] * inv, acc_o[qb][db][4 * g + 1] * inv}, e16x2);
+          e16x2 up = __builtin_convertvector((f32x2){acc_o[qb][db][4 * g + 2] * inv, acc_o[qb][db][4 * g + 3] * inv}, e16x2);
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          *(u32x2*)(orow + db * 32 + 8 * g + 4 * hi) =
+              (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, up)};
+        }
+      if (hi == 0) {
+        const float lse = (l_tot > 0.f) ? kLn2 * (ref[qb] + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
+        p.lse[(int64_t)bh * N + qrow] = lse;
+      }
+    }
+  }
+  if (grp == 0) phase_end(false);            // G0 matches G1's barrier count
+}
+
+// ------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------
 
 // Compiled tile shapes: block_m query rows per workgroup (NW waves x QB blocks of
 // 32 queries per wave) and block_n keys per K/V tile.
-struct TileShape { int bm, bn, nw, qb; };
-constexpr TileShape kTiles[] = {{64, 64, 2, 1}, {128, 64, 4, 1}, {256, 64, 4, 2},
-                                 {128, 32, 4, 1}, {256, 32, 4, 2}};
+struct TileShape { int bm, bn, nw, qb; bool d128; };
+constexpr TileShape kTiles[] = {
+    // fa_fwd_kernel: 2 or 4 waves, each owning 32 query rows
+    {64, 64, 2, 1, true}, {128, 64, 4, 1, true}, {128, 32, 4, 1, true},
+    // fa_fwd_pp_kernel: 8 waves in two groups taking turns on each SIMD's matrix pipe
+    {256, 32, 8, 1, true}, {256, 64, 8, 1, false}, {512, 32, 8, 2, false}};
 
 template <int D, bool BF16, bool CAUSAL, int NW, int QB, int BN>
 hipError_t launch_one(const Params& p, hipStream_t stream) {
   hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, NW, QB, BN>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16, bool CAUSAL, int QB, int BN>
+hipError_t launch_pp(const Params& p, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_fwd_pp_kernel<D, BF16, CAUSAL, QB, BN>), dim3(p.total_wgs), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -481,10 +880,11 @@ hipError_t launch_tile(const Params& p, int bm, int bn, hipStream_t stream) {
   if (bm == 64 && bn == 64) return launch_one<D, BF16, CAUSAL, 2, 1, 64>(p, stream);
   if (bm == 128 && bn == 64) return launch_one<D, BF16, CAUSAL, 4, 1, 64>(p, stream);
   if (bm == 128 && bn == 32) return launch_one<D, BF16, CAUSAL, 4, 1, 32>(p, stream);
+  if (bm == 256 && bn == 32) return launch_pp<D, BF16, CAUSAL, 1, 32>(p, stream);
   if constexpr (D == 64) {
-    // two query blocks per wave: at d = 128 their accumulators do not fit the budget
-    if (bm == 256 && bn == 64) return launch_one<D, BF16, CAUSAL, 4, 2, 64>(p, stream);
-    if (bm == 256 && bn == 32) return launch_one<D, BF16, CAUSAL, 4, 2, 32>(p, stream);
+    // at d = 128 these fragments and accumulators do not fit 256 registers
+    if (bm == 256 && bn == 64) return launch_pp<D, BF16, CAUSAL, 1, 64>(p, stream);
+    if (bm == 512 && bn == 32) return launch_pp<D, BF16, CAUSAL, 2, 32>(p, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -498,7 +898,7 @@ hipError_t launch_d(const Params& p, bool bf16, bool causal, int bm, int bn, hip
 bool tile_ok(int64_t d, int bm, int bn) {
   if (d != 64 && d != 128) return false;
   for (const TileShape& t : kTiles)
-    if (t.bm == bm && t.bn == bn) return !(d == 128 && t.qb > 1);
+    if (t.bm == bm && t.bn == bn) return d == 64 || t.d128;
   return false;
 }
 
@@ -546,21 +946,21 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
 }
 
 void default_tile(int64_t N, int64_t d, int causal, int* bm, int* bn) {
-  // Measured on MI355X (one tile sweep per workload family):
+  // Measured on MI355X (tile sweeps per workload family):
   //  - short sequences: the smallest tile, so that more workgroups exist;
-  //  - d = 64, non-causal: two 32-query blocks per wave share every K/V fragment
-  //    read (half the LDS traffic per MFMA), 32-key tiles keep it within 256 VGPRs;
-  //  - d = 128, non-causal: one block per wave, 32-key tiles (no spills);
-  //  - causal: one block per wave (row blocks of uneven length balance better);
-  //    64-key tiles at d = 64, 32-key tiles at d = 128 (no spills).
+  //  - causal: the four-wave kernel with one 32-query block per wave (row blocks of
+  //    uneven length balance better); 64-key tiles at d = 64, 32-key at d = 128;
+  //  - non-causal: the eight-wave kernel, two 32-query blocks per wave at d = 64
+  //    (every K and V^T fragment read feeds two MFMAs), one at d = 128 (two do not
+  //    fit 256 registers); 32-key tiles.
   if (N <= 128) {
     *bm = 64;
     *bn = 64;
-  } else if (causal) {
+  } else if (causal || N <= 256) {
     *bm = 128;
     *bn = (d == 64) ? 64 : 32;
   } else {
-    *bm = (d == 64) ? 256 : 128;
+    *bm = (d == 64) ? 512 : 256;
     *bn = 32;
   }
 }

@@ -22,7 +22,9 @@ pytestmark = pytest.mark.gpu
 TOL_O = {"f16": 2e-3, "bf16": 1e-2}
 TOL_LSE = 1e-3
 TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
-ALL_TILES = [(64, 64), (128, 64), (256, 64), (128, 32), (256, 32)]
+ALL_TILES = [(64, 64), (128, 64), (128, 32), (256, 32), (256, 64), (512, 32)]
+# eight-wave tiles (two groups of four waves taking turns on each SIMD)
+PP_TILES = [(256, 32), (256, 64), (512, 32)]
 
 
 def _say(msg):
@@ -183,6 +185,21 @@ def test_every_tile_shape(tile, d):
         q, k, v = make_random(1, 4, 333, d, dtype, seed=tile[0] + d)
         for causal in (False, True):
             check_against_oracle(q, k, v, 0.09, causal, dtype, tile=tile, label=f"tile {tile}")
+
+
+@pytest.mark.parametrize("N", [1, 31, 32, 33, 64, 95, 257, 511, 513, 1000])
+@pytest.mark.parametrize("tile", PP_TILES)
+@pytest.mark.parametrize("d", [64, 128])
+def test_pp_tiles_edge_sizes(N, tile, d):
+    """The eight-wave tiles at sizes where a workgroup has one, two or three key tiles,
+    waves whose rows start past N, and ragged last tiles."""
+    if not fa.fa_tile_supported(d, *tile):
+        pytest.skip(f"tile {tile} is not compiled for d={d}")
+    for dtype in ("f16", "bf16"):
+        q, k, v = make_random(1, 3, N, d, dtype, seed=N * 3 + tile[0] + tile[1] + d)
+        for causal in (False, True):
+            check_against_oracle(q, k, v, 1 / math.sqrt(d), causal, dtype, tile=tile,
+                                 label=f"pp N={N} tile {tile}")
 
 
 def test_large_scores_rescaling():
