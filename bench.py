@@ -75,12 +75,12 @@ def _pmc_rows(d, counter):
             if row["Counter_Name"] != counter:
                 continue
             name = row["Kernel_Name"]
-            if "fa_fwd_kernel" in name:
+            if "fa_fwd_kernel" in name or "fa_fwd_pp_kernel" in name:
                 fa_vals.append((name, float(row["Counter_Value"])))
             elif "copyBuffer" in name:
                 copy_vals.append(float(row["Counter_Value"]))
     if not fa_vals or not copy_vals:
-        raise SystemExit(f"{d}: missing fa_fwd_kernel or copy dispatches for {counter}")
+        raise SystemExit(f"{d}: missing attention-kernel or copy dispatches for {counter}")
     return fa_vals, copy_vals
 
 

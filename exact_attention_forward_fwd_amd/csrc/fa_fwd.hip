@@ -8,10 +8,14 @@
 //      holding one query's scores for 16 keys of every 32-key block, so the
 //      row (per-query) reductions are in-lane ops plus one permlane32 swap;
 //   2. masks the causal diagonal / ragged tail to -inf (only on tiles that need it);
-//   3. updates the online-softmax state in registers: the row maximum moves the
-//      exponent reference ref = fl(c m) only when it grows past ref + 8 (log2 units),
-//      rescaling l and U by alpha = 2^(ref_old - ref_new) then; the weights are
-//      P = 2^(c x - ref) with c = s log2(e) folded into one FMA, l' = l + rowsum P;
+//   3. updates the online-softmax state in registers. The weights are formed against
+//      the current exponent reference, P = 2^(c x - ref) with c = s log2(e) folded
+//      into one FMA, and their per-lane sum both updates l and checks the reference:
+//      while it stays at most 2^8, so does every weight. On a row's first tile, or
+//      when a sum exceeds 2^8 (a new maximum well above the reference), the tile is
+//      redone after moving the reference up to the row maximum, ref = fl(c m), and
+//      rescaling l and U by alpha = 2^(ref_old - ref_new). No row maximum is needed
+//      on the common path;
 //   4. rounds P to 16 bits in registers; those registers are directly the B
 //      operand of O^T += V^T P^T (the key order inside each 16-key MFMA step is
 //      permuted identically on both operands, which a sum over keys allows), issued
@@ -87,22 +91,11 @@ struct Params {
   float c;            // scale * log2(e)
 };
 
-// Exponent headroom (log2 units) before the softmax reference is moved. The
-// weights of a tile are 2^(c x - ref) with ref = fl(c m_ref); keeping ref while the
-// running maximum stays within TAU of it leaves every weight <= 2^TAU (256, far
-// inside fp16's range) and skips the rescale of l and U on almost every tile. The
-// final O = U / l and LSE = ln2 (ref + log2 l) hold for any common reference.
-constexpr float kTau = 8.0f;
-#ifndef PP_VALU_PRIO
-#define PP_VALU_PRIO 0
-#endif
-#ifndef PP_MFMA_PRIO
-#define PP_MFMA_PRIO 0
-#endif
-constexpr int kPpValuPrio = PP_VALU_PRIO;
-constexpr int kPpMfmaPrio = PP_MFMA_PRIO;
-// The ping-pong kernel keeps its reference while a lane's weights of one tile sum to
-// at most this (so each weight is at most 2^kTau as well).
+// The softmax keeps its exponent reference while a lane's weights of one tile sum to
+// at most this, which bounds every weight by it as well (2^8, far inside fp16's
+// range). The final O = U / l and LSE = ln2 (ref + log2 l) hold for any common
+// reference, so keeping it, instead of moving it on every new maximum, changes
+// nothing but rounding.
 constexpr float kSumMax = 256.0f;
 
 // The P V MFMAs are issued at raised wave priority: the SIMD's other wave then gets
@@ -265,9 +258,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   // ref = fl(c m_ref) (kept as the rounded product itself, so that
   // alpha = 2^(ref_old - ref_new) is exactly 1 for a row whose reference did not
   // move) and this lane's share of l.
-  float ref[QB], l_run[QB];
+  float ref[QB], nb[QB], l_run[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { ref[qb] = -INFINITY; l_run[qb] = 0.f; }
+  for (int qb = 0; qb < QB; ++qb) { ref[qb] = -INFINITY; nb[qb] = 0.f; l_run[qb] = 0.f; }
   i16x8 pprev[QB][BN / 16];   // P of the previous tile as 16-bit B operands
 
   // Tiles [0, n_full) need no mask for any query of this workgroup; the rest
@@ -334,25 +327,47 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     }
 
     // ---- online softmax ----
-    bool move[QB];
-    float cand[QB];
-    bool any_move = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-      mx = max_halves(mx);
-      cand[qb] = mx * c;                     // fl(c * tile max), -inf if nothing valid
-      move[qb] = cand[qb] > ref[qb] + kTau;  // new reference needed for this query
-      any_move |= move[qb];
-    }
-    if (__builtin_amdgcn_ballot_w64(any_move)) {   // wave-uniform: rare after the first tiles
+    // Weights against the current reference; their per-lane sum updates l and checks
+    // the reference (the same rule as the eight-wave kernel's softmax: redo the tile
+    // with references moved to the row maxima when a sum exceeds kSumMax, or on a
+    // row's first tile).
+    auto weights = [&](float (&rs)[QB]) __attribute__((always_inline)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float ref_new = move[qb] ? cand[qb] : ref[qb];
+        float part[2] = {0.f, 0.f};
+#pragma unroll
+        for (int tt = 0; tt < BN / 16; ++tt) {
+          const int kb = tt >> 1, base = 8 * (tt & 1);
+          float e[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + i], c, nb[qb]));
+          e16x2 h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[i] = __builtin_convertvector((f32x2){e[2 * i], e[2 * i + 1]}, e16x2);
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          pprev[qb][tt] = __builtin_bit_cast(i16x8, ((u32x4){__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
+                                                              __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])}));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) part[i & 1] += e[i];
+        }
+        rs[qb] = part[0] + part[1];
+      }
+    };
+    float rs[QB];
+    weights(rs);
+    bool redo = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) redo |= !(rs[qb] <= kSumMax) || ref[qb] == -INFINITY;
+    if (__builtin_amdgcn_ballot_w64(redo)) {   // wave-uniform: rare after the first tile
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
+        const float cand = max_halves(mx) * c;
+        const float ref_new = cand > ref[qb] ? cand : ref[qb];
         const float alpha = __builtin_amdgcn_exp2f(ref[qb] - ref_new);   // 1 exactly if unmoved, 0 from -inf
         l_run[qb] *= alpha;
 #pragma unroll
@@ -360,35 +375,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc_o[qb][db][r] *= alpha;    // after the pending P V landed
         ref[qb] = ref_new;
+        nb[qb] = (ref_new == -INFINITY) ? 0.f : -ref_new;
       }
+      weights(rs);
     }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // -inf guard: while a row has seen no valid key, use 0 as the exponent base
-      const float neg_base = (ref[qb] == -INFINITY) ? 0.f : -ref[qb];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][r], c, neg_base));
-          s[qb][kb][r] = e;
-          rs += e;
-        }
-      l_run[qb] += rs;
-      // P^T as 16-bit B operands: step tt covers s[qb][tt/2][8 (tt%2) .. +7]
-#pragma unroll
-      for (int tt = 0; tt < BN / 16; ++tt) {
-        const int kb = tt >> 1, base = 8 * (tt & 1);
-        e16x2 h0 = __builtin_convertvector((f32x2){s[qb][kb][base + 0], s[qb][kb][base + 1]}, e16x2);
-        e16x2 h1 = __builtin_convertvector((f32x2){s[qb][kb][base + 2], s[qb][kb][base + 3]}, e16x2);
-        e16x2 h2 = __builtin_convertvector((f32x2){s[qb][kb][base + 4], s[qb][kb][base + 5]}, e16x2);
-        e16x2 h3 = __builtin_convertvector((f32x2){s[qb][kb][base + 6], s[qb][kb][base + 7]}, e16x2);
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        pprev[qb][tt] = __builtin_bit_cast(i16x8, ((u32x4){__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
-                                                            __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3)}));
-      }
-    }
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
   };
 
   // LDS stores by other waves' direct loads become visible after this wave's own
@@ -668,17 +660,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // its result is unused (S of a tile past this wave's rows) or zero (P is zero
   // before the first tile and after the wave's last one).
   auto m_cluster = [&]() __attribute__((always_inline)) {
-    if constexpr (kPpMfmaPrio != 0) __builtin_amdgcn_s_setprio(kPpMfmaPrio);
 #pragma unroll
     for (int i = 0; i < NQK; ++i) { qk_step(i); pv_step(i); }
-    if constexpr (kPpMfmaPrio != 0) __builtin_amdgcn_s_setprio(0);
   };
 
   // Softmax of tile j (keys n0..n0+BN) in s, into pk; l, ref and (rarely) U updated.
   // The common path needs no row maximum: the weights are formed against the current
   // reference, P = 2^(c x + nb) with nb = -ref, and their per-lane sum both updates l
   // and checks the reference. While every lane's sum of this tile's weights is at
-  // most 2^kTau, every weight is too (and far inside fp16's range). Otherwise (a new
+  // most kSumMax, every weight is too (and far inside fp16's range). Otherwise (a new
   // maximum well above the reference, an infinite weight, or the first tile, whose
   // reference is still -inf) the wave takes the rare path: each query's reference
   // moves up to its row maximum, l and U are scaled by alpha = 2^(ref_old - ref_new),
@@ -767,7 +757,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // stage holding no needed tile is read harmlessly), then the softmax, or P = 0
   // for a tile this wave does not compute.
   auto v_cluster = [&](int j, const short* k_next, const short* v_cur) __attribute__((always_inline)) {
-    if constexpr (kPpValuPrio != 0) __builtin_amdgcn_s_setprio(kPpValuPrio);
     read_k(k_next);
     read_v(v_cur);
     if (j < Tw) {
@@ -779,7 +768,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int tt = 0; tt < NTT; ++tt) pk[qb][tt] = (i16x8){};
     }
     pin_softmax_state();
-    if constexpr (kPpValuPrio != 0) __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- prologue: K(0), V(0), K(1) in LDS; K(0) fragments in registers ----
@@ -946,21 +934,21 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
 }
 
 void default_tile(int64_t N, int64_t d, int causal, int* bm, int* bn) {
-  // Measured on MI355X (tile sweeps per workload family):
+  // Measured on MI355X (interleaved tile sweeps per workload family):
   //  - short sequences: the smallest tile, so that more workgroups exist;
-  //  - causal: the four-wave kernel with one 32-query block per wave (row blocks of
-  //    uneven length balance better); 64-key tiles at d = 64, 32-key at d = 128;
-  //  - non-causal: the eight-wave kernel, two 32-query blocks per wave at d = 64
-  //    (every K and V^T fragment read feeds two MFMAs), one at d = 128 (two do not
-  //    fit 256 registers); 32-key tiles.
+  //  - causal, and d = 64: the four-wave kernel with one 32-query block per wave
+  //    (causal row blocks of uneven length balance better with small blocks);
+  //    64-key tiles for long non-causal d = 64, 32-key tiles otherwise;
+  //  - long non-causal d = 128: the eight-wave kernel (one wave of each SIMD pair
+  //    issues MFMAs while the other runs its softmax), 32-key tiles.
   if (N <= 128) {
     *bm = 64;
     *bn = 64;
-  } else if (causal || N <= 256) {
+  } else if (causal || d == 64 || N <= 256) {
     *bm = 128;
-    *bn = (d == 64) ? 64 : 32;
+    *bn = (d == 64 && !causal && N > 256) ? 64 : 32;
   } else {
-    *bm = (d == 64) ? 512 : 256;
+    *bm = 256;
     *bn = 32;
   }
 }
