@@ -510,10 +510,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                           _Float16 __attribute__((ext_vector_type(2)))>::type;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-  __shared__ __attribute__((aligned(1024))) short lds_k0[TILE];
-  __shared__ __attribute__((aligned(1024))) short lds_k1[TILE];
-  __shared__ __attribute__((aligned(1024))) short lds_v0[TILE];
-  __shared__ __attribute__((aligned(1024))) short lds_v1[TILE];
+  // One LDS array holding the four stages: with the loop unrolled by two each stage
+  // is a compile-time offset that folds into the read instructions, so the fragment
+  // addresses need one register each, not one per stage. (One object is enough here:
+  // no wave reads LDS while one of its own direct loads is pending.)
+  __shared__ __attribute__((aligned(1024))) short lds[4 * TILE];
+  short* const lds_k0 = lds;
+  short* const lds_k1 = lds + TILE;
+  short* const lds_v0 = lds + 2 * TILE;
+  short* const lds_v1 = lds + 3 * TILE;
 
   // ---- work item (XCD-contiguous, causal heavy-first) ----
   const int bid = blockIdx.x;
