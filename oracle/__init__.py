@@ -93,12 +93,25 @@ def _shape3(q, k, v):
     return lead, bh, nq, nk, d
 
 
-def attention_fwd(q, k, v, scale: float, causal: bool = False, lib=None):
+ALIGNMENTS = {"top-left": 1, "bottom-right": 2}
+
+
+def _causal_mode(causal, align: str) -> int:
+    if not causal:
+        return 0
+    if align not in ALIGNMENTS:
+        raise ValueError(f"align must be one of {sorted(ALIGNMENTS)}")
+    return ALIGNMENTS[align]
+
+
+def attention_fwd(q, k, v, scale: float, causal: bool = False, lib=None, align: str = "top-left"):
     """Exact attention forward in fp64 over every row.
 
     q: [..., Nq, d]; k, v: [..., Nk, d] (any float dtype, upcast losslessly to fp64).
     Returns (o [..., Nq, d] float64, lse [..., Nq] float64), LSE in natural log of the
-    scaled scores. Causal masking is top-left aligned (key j valid iff j <= i).
+    scaled scores. Causal masking is top-left aligned by default (key j valid iff
+    j <= i); ``align="bottom-right"`` makes key j valid iff j <= i + Nk - Nq. A row
+    with no valid key gets O = 0 and LSE = -inf.
     ``lib`` selects another build of the oracle source (default: liboracle.so).
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
@@ -106,14 +119,14 @@ def attention_fwd(q, k, v, scale: float, causal: bool = False, lib=None):
     o = np.empty(lead + (nq, d), dtype=np.float64)
     lse = np.empty(lead + (nq,), dtype=np.float64)
     rc = (lib or _load()).oracle_attn_fwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                              bh, nq, nk, d, float(scale), int(bool(causal)))
+                                              bh, nq, nk, d, float(scale), _causal_mode(causal, align))
     if rc != 0:
         raise ValueError(f"oracle_attn_fwd_f64 failed with code {rc}")
     return o, lse
 
 
-def attention_rows(q, k, v, scale: float, causal: bool, rows, lib=None):
-    """Exact fp64 outputs for selected rows only.
+def attention_rows(q, k, v, scale: float, causal: bool, rows, lib=None, align: str = "top-left"):
+    """Exact fp64 outputs for selected rows only (masking as in ``attention_fwd``).
 
     ``rows`` holds flat row indices bh*Nq + i. Returns (o [len(rows), d], lse [len(rows)]).
     """
@@ -123,7 +136,7 @@ def attention_rows(q, k, v, scale: float, causal: bool, rows, lib=None):
     o = np.empty((rows.size, d), dtype=np.float64)
     lse = np.empty((rows.size,), dtype=np.float64)
     rc = (lib or _load()).oracle_attn_rows_f64(
-        _ptr(q), _ptr(k), _ptr(v), bh, nq, nk, d, float(scale), int(bool(causal)),
+        _ptr(q), _ptr(k), _ptr(v), bh, nq, nk, d, float(scale), _causal_mode(causal, align),
         rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), rows.size, _ptr(o), _ptr(lse))
     if rc != 0:
         raise ValueError(f"oracle_attn_rows_f64 failed with code {rc}")

@@ -24,10 +24,13 @@
  *   l = sum exp(z_j - m),  O = (sum exp(z_j - m) V_j) / l,  LSE = m + ln l,
  * which equals s*m_raw + ln l of the blog's final section because s > 0.
  *
- * Causal masking is top-left aligned: key j is valid for query i iff j <= i
- * (the blog's causal section, Fig. 11). With that alignment key 0 is valid for
- * every query, so a row can have no valid key only when Nk = 0; such a row gets
- * O = 0 and LSE = -inf (the limit of an empty sum; the pages leave the case open).
+ * Causal masking (argument `causal`): 0 = none; 1 = top-left aligned, key j is
+ * valid for query i iff j <= i (the blog's causal section, Fig. 11); 2 =
+ * bottom-right aligned, key j valid iff j <= i + Nk - Nq, the other alignment that
+ * section names as differing from top-left only when the query and key lengths
+ * differ (the last query sees every key). A row with no valid key (Nk = 0, or
+ * bottom-right with i < Nq - Nk) gets O = 0 and LSE = -inf (the limit of an
+ * empty sum; the pages leave the case open).
  *
  * Arithmetic: IEEE double, libm exp/log, compiled without fast-math, so the
  * sums are evaluated strictly in loop order.
@@ -43,10 +46,14 @@
 /* One output row. z is caller scratch of length Nk. Returns nothing; writes
  * o_row[0..d) and *lse_out. */
 static void oracle_one_row(const double* q_row, const double* k, const double* v,
-                           int64_t Nk, int64_t d, double scale, int causal, int64_t i,
-                           double* z, double* o_row, double* lse_out) {
+                           int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
+                           int64_t i, double* z, double* o_row, double* lse_out) {
   int64_t nvalid = Nk;
-  if (causal) nvalid = (i + 1 < Nk) ? (i + 1) : Nk;   /* keys 0..i are valid */
+  if (causal == 1) nvalid = (i + 1 < Nk) ? (i + 1) : Nk;   /* keys 0..i are valid */
+  if (causal == 2) {                                       /* keys 0..i+Nk-Nq are valid */
+    const int64_t last = i + Nk - Nq;
+    nvalid = (last + 1 < Nk) ? (last + 1) : Nk;
+  }
   if (nvalid <= 0) {
     for (int64_t c = 0; c < d; ++c) o_row[c] = 0.0;
     *lse_out = -INFINITY;
@@ -78,9 +85,10 @@ static void oracle_one_row(const double* q_row, const double* k, const double* v
 
 static int oracle_check_args(const void* q, const void* k, const void* v, const void* o,
                              const void* lse, int64_t BH, int64_t Nq, int64_t Nk, int64_t d,
-                             double scale) {
+                             double scale, int causal) {
   if (BH < 0 || Nq < 0 || Nk < 0 || d < 0) return 2;
   if (!(scale > 0.0) || !isfinite(scale)) return 3;
+  if (causal < 0 || causal > 2) return 6;
   if (BH * Nq == 0) return 0;
   if (!q || !o || !lse) return 1;
   if (Nk > 0 && (!k || !v)) return 1;
@@ -89,13 +97,14 @@ static int oracle_check_args(const void* q, const void* k, const void* v, const 
 
 /* Full forward over every row.
  * q: [BH, Nq, d], k, v: [BH, Nk, d], o: [BH, Nq, d], lse: [BH, Nq]; all row-major
- * contiguous doubles, owned by the caller. Returns 0 on success, 1 for a null
- * pointer, 2 for a negative size, 3 for a scale that is not finite and > 0,
- * 4 when scratch memory cannot be allocated. */
+ * contiguous doubles, owned by the caller. causal: 0, 1 (top-left) or 2
+ * (bottom-right). Returns 0 on success, 1 for a null pointer, 2 for a negative
+ * size, 3 for a scale that is not finite and > 0, 4 when scratch memory cannot be
+ * allocated, 6 for an unknown causal mode. */
 int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, double* o,
                         double* lse, int64_t BH, int64_t Nq, int64_t Nk, int64_t d,
                         double scale, int causal) {
-  int rc = oracle_check_args(q, k, v, o, lse, BH, Nq, Nk, d, scale);
+  int rc = oracle_check_args(q, k, v, o, lse, BH, Nq, Nk, d, scale, causal);
   if (rc || BH * Nq == 0) return rc;
   int fail = 0;
 #pragma omp parallel
@@ -108,7 +117,7 @@ int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, doubl
 #pragma omp for schedule(dynamic, 8)
       for (int64_t r = 0; r < BH * Nq; ++r) {
         int64_t bh = r / Nq, i = r % Nq;
-        oracle_one_row(q + r * d, k + bh * Nk * d, v + bh * Nk * d, Nk, d, scale, causal, i, z,
+        oracle_one_row(q + r * d, k + bh * Nk * d, v + bh * Nk * d, Nq, Nk, d, scale, causal, i, z,
                        o + r * d, lse + r);
       }
       free(z);
@@ -123,7 +132,7 @@ int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, doubl
 int oracle_attn_rows_f64(const double* q, const double* k, const double* v, int64_t BH,
                          int64_t Nq, int64_t Nk, int64_t d, double scale, int causal,
                          const int64_t* rows, int64_t nrows, double* o_rows, double* lse_rows) {
-  int rc = oracle_check_args(q, k, v, o_rows, lse_rows, BH, Nq, Nk, d, scale);
+  int rc = oracle_check_args(q, k, v, o_rows, lse_rows, BH, Nq, Nk, d, scale, causal);
   if (rc) return rc;
   if (nrows <= 0) return 0;
   if (!rows) return 1;
@@ -141,7 +150,7 @@ int oracle_attn_rows_f64(const double* q, const double* k, const double* v, int6
       for (int64_t t = 0; t < nrows; ++t) {
         int64_t r = rows[t];
         int64_t bh = r / Nq, i = r % Nq;
-        oracle_one_row(q + r * d, k + bh * Nk * d, v + bh * Nk * d, Nk, d, scale, causal, i, z,
+        oracle_one_row(q + r * d, k + bh * Nk * d, v + bh * Nk * d, Nq, Nk, d, scale, causal, i, z,
                        o_rows + t * d, lse_rows + t);
       }
       free(z);

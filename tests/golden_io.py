@@ -29,8 +29,8 @@ def load_worked_example():
         raw = json.load(f)
     out = {}
     for key, ent in raw.items():
-        if key == "causal":
-            out["causal"] = {k: _arr(v["value"]) for k, v in ent.items()}
+        if key in ("causal", "bottom_right"):
+            out[key] = {k: _arr(v["value"]) for k, v in ent.items()}
         elif isinstance(ent, dict) and "value" in ent:
             v = ent["value"]
             out[key] = _arr(v) if isinstance(v, list) else _val(v)

@@ -43,6 +43,38 @@ def pin_worked_example_causal(fwd):
     np.testing.assert_allclose(lse, g["causal"]["LSE"], rtol=0, atol=1e-14)
 
 
+def pin_worked_example_bottom_right(fwd):
+    q, k, v, g = _example()
+    o, lse = fwd(q, k, v, LN2, True, align="bottom-right")
+    np.testing.assert_allclose(o, g["bottom_right"]["O"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, g["bottom_right"]["LSE"], rtol=0, atol=1e-14)
+
+
+def pin_bottom_right_reductions(fwd):
+    """Bottom-right causal reduces to known cases: with Nq = Nk it is top-left; a
+    single query sees every key (non-causal); with Nq > Nk the first Nq - Nk rows
+    have no valid key (O = 0, LSE = -inf) and row i >= Nq - Nk is top-left row
+    i - (Nq - Nk)."""
+    rng = np.random.default_rng(21)
+    d, s = 6, 0.45
+    K = rng.standard_normal((9, d)); V = rng.standard_normal((9, d))
+    Q = rng.standard_normal((9, d))
+    o_br, l_br = fwd(Q, K, V, s, True, align="bottom-right")
+    o_tl, l_tl = fwd(Q, K, V, s, True)
+    np.testing.assert_array_equal(o_br, o_tl)
+    np.testing.assert_array_equal(l_br, l_tl)
+    o1, l1 = fwd(Q[4:5], K, V, s, True, align="bottom-right")
+    o2, l2 = fwd(Q[4:5], K, V, s, False)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    Qb = rng.standard_normal((13, d))
+    o3, l3 = fwd(Qb, K, V, s, True, align="bottom-right")
+    assert np.all(o3[:4] == 0.0) and np.all(np.isneginf(l3[:4]))
+    o4, l4 = fwd(Qb[4:], K, V, s, True)
+    np.testing.assert_array_equal(o3[4:], o4)
+    np.testing.assert_array_equal(l3[4:], l4)
+
+
 def pin_embedded_example(fwd):
     """The worked example as a square N=4 problem with d padded to 64 by zeros and
     query rows 2,3 set to 0 (the form the GPU parity test uses). Rows 0,1 keep the
@@ -102,15 +134,19 @@ def pin_against_scipy(fwd):
     scaled score matrix built with numpy (masked entries -inf for causal)."""
     rng = np.random.default_rng(3)
     for (nq, nk, d, causal) in [(1, 1, 1, False), (3, 5, 2, False), (7, 7, 4, True),
-                                (9, 9, 16, False), (6, 11, 5, True), (33, 33, 8, True)]:
-        if causal and nq > nk:
-            continue
+                                (9, 9, 16, False), (6, 11, 5, True), (33, 33, 8, True),
+                                (6, 11, 5, "bottom-right"), (1, 9, 3, "bottom-right"),
+                                (10, 10, 4, "bottom-right")]:
         Q = rng.standard_normal((nq, d)); K = rng.standard_normal((nk, d))
         V = rng.standard_normal((nk, d)); s = 1.0 / math.sqrt(d)
         z = s * (Q @ K.T)
+        off = (nk - nq) if causal == "bottom-right" else 0
         if causal:
-            z = np.where(np.arange(nk)[None, :] <= np.arange(nq)[:, None], z, -np.inf)
-        o, lse = fwd(Q, K, V, s, causal)
+            z = np.where(np.arange(nk)[None, :] <= np.arange(nq)[:, None] + off, z, -np.inf)
+        if causal == "bottom-right":
+            o, lse = fwd(Q, K, V, s, True, align="bottom-right")
+        else:
+            o, lse = fwd(Q, K, V, s, causal)
         np.testing.assert_allclose(o, scipy.special.softmax(z, axis=1) @ V, rtol=1e-12, atol=1e-13)
         np.testing.assert_allclose(lse, scipy.special.logsumexp(z, axis=1), rtol=1e-13, atol=1e-13)
 
@@ -171,13 +207,14 @@ def pin_heads_independent(fwd):
         assert not np.allclose(o2[1, 2], o[1, 2])
 
 
-ALL_PINS = [pin_worked_example, pin_worked_example_causal, pin_embedded_example,
+ALL_PINS = [pin_worked_example, pin_worked_example_causal, pin_worked_example_bottom_right,
+            pin_bottom_right_reductions, pin_embedded_example,
             pin_zero_query_prefix_mean, pin_one_hot_limit, pin_against_scipy, pin_invariants,
             pin_heads_independent]
 
 
 def _fwd(lib=None):
-    return lambda q, k, v, s, c: oracle.attention_fwd(q, k, v, s, c, lib=lib)
+    return lambda q, k, v, s, c, align="top-left": oracle.attention_fwd(q, k, v, s, c, lib=lib, align=align)
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -214,12 +251,14 @@ def test_degenerate_sizes_and_errors():
 MUTATIONS = {
     "drop_scale": ("z[j] = scale * x;", "z[j] = x;"),
     "causal_off_by_one": ("nvalid = (i + 1 < Nk) ? (i + 1) : Nk;", "nvalid = (i < Nk) ? i : Nk;"),
+    "bottom_right_sign": ("const int64_t last = i + Nk - Nq;", "const int64_t last = i - Nk + Nq;"),
+    "bottom_right_off_by_one": ("nvalid = (last + 1 < Nk) ? (last + 1) : Nk;", "nvalid = (last < Nk) ? last : Nk;"),
     "k_for_v": ("const double* k_row = k + j * d;", "const double* k_row = v + j * d;"),
     "lse_without_max": ("*lse_out = m + log(l);", "*lse_out = log(l);"),
     "exp_sign": ("l += exp(z[j] - m);", "l += exp(m - z[j]);"),
     "no_normalisation": ("double p = exp(z[j] - m) / l;", "double p = exp(z[j] - m);"),
-    "first_head_v": ("k + bh * Nk * d, v + bh * Nk * d, Nk, d, scale, causal, i, z,\n"
-                     "                       o + r * d", "k + bh * Nk * d, v, Nk, d, scale, causal, i, z,\n"
+    "first_head_v": ("k + bh * Nk * d, v + bh * Nk * d, Nq, Nk, d, scale, causal, i, z,\n"
+                     "                       o + r * d", "k + bh * Nk * d, v, Nq, Nk, d, scale, causal, i, z,\n"
                      "                       o + r * d"),
     "dot_drops_last_term": ("for (int64_t c = 0; c < d; ++c) x += q_row[c] * k_row[c];",
                             "for (int64_t c = 0; c + 1 < d; ++c) x += q_row[c] * k_row[c];"),
