@@ -18,9 +18,9 @@ FA_BF16 = 1
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED_HEADDIM",
     4: "FA_ERR_BAD_SCALE", 5: "FA_ERR_BAD_DTYPE", 6: "FA_ERR_MISALIGNED", 7: "FA_ERR_TOO_LARGE",
-    8: "FA_ERR_UNSUPPORTED_TILE", 9: "FA_ERR_HIP",
+    8: "FA_ERR_UNSUPPORTED_TILE", 9: "FA_ERR_HIP", 10: "FA_ERR_BAD_STRIDE",
 }
-EXPORTED = ("fa_fwd", "fa_fwd_tiled", "fa_tile_supported", "fa_default_tile", "fa_status_str")
+EXPORTED = ("fa_fwd", "fa_fwd_tiled", "fa_fwd_ex", "fa_tile_supported", "fa_default_tile", "fa_status_str")
 
 
 class FaError(RuntimeError):
@@ -47,6 +47,10 @@ def load_library(path: str = LIB_PATH):
     lib.fa_fwd.restype = i32
     lib.fa_fwd_tiled.argtypes = common + [i32, i32]
     lib.fa_fwd_tiled.restype = i32
+    i64p = ctypes.POINTER(i64)
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p,
+                              ctypes.c_float, i32, i32, vp, i32, i32]
+    lib.fa_fwd_ex.restype = i32
     lib.fa_tile_supported.argtypes = [i64, i32, i32]
     lib.fa_tile_supported.restype = i32
     lib.fa_default_tile.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -70,6 +74,21 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream) -> int:
 def fa_fwd_tiled(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream, block_m, block_n) -> int:
     return load_library().fa_fwd_tiled(q, k, v, o, lse, B, H, N, d, scale, int(causal), dtype,
                                        stream, block_m, block_n)
+
+
+def _strides(st):
+    """{batch, head, row} element strides as a C array, or NULL for None."""
+    if st is None:
+        return None
+    return (ctypes.c_int64 * 3)(*[int(x) for x in st])
+
+
+def fa_fwd_ex(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, q_strides, k_strides, v_strides, o_strides,
+              scale, causal, dtype, stream, block_m=0, block_n=0) -> int:
+    """Raw C call of the general entry point; strides are 3-sequences or None."""
+    return load_library().fa_fwd_ex(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, _strides(q_strides),
+                                    _strides(k_strides), _strides(v_strides), _strides(o_strides),
+                                    scale, int(causal), dtype, stream, int(block_m), int(block_n))
 
 
 def fa_tile_supported(d: int, block_m: int, block_n: int) -> bool:
@@ -131,4 +150,48 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, block_m: int 
         st = fa_fwd_tiled(*args, int(block_m), int(block_n))
     if st != 0:
         raise FaError(st, "fa_fwd")
+    return out, lse
+
+
+def fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, block_m: int | None = None,
+           block_n: int | None = None, out=None, lse=None, stream=None):
+    """General attention forward on torch tensors: q [B, Hq, Nq, d], k and v [B, Hk, Nk, d]
+    with any strides whose last dimension is contiguous; Hq a multiple of Hk (query
+    head h reads K/V head h // (Hq // Hk)). ``causal`` masks key j > i + Nk - Nq
+    (bottom-right alignment). Returns (o, lse): o [B, Hq, Nq, d] laid out like q
+    unless ``out`` is given, lse float32 [B, Hq, Nq] contiguous.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, heads, N, d]")
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name}'s last dimension must be contiguous")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    B, Hq, Nq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must be [B, Hk, Nk, d] with q's B and d")
+    Hk, Nk = k.shape[1], k.shape[2]
+    dt = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.stride(-1) != 1:
+        raise ValueError("out must be shaped like q with a contiguous last dimension")
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hk,
+                   Nq, Nk, d, q.stride()[:3], k.stride()[:3], v.stride()[:3], out.stride()[:3],
+                   float(scale), causal, dt, sp, block_m or 0, block_n or 0)
+    if st != 0:
+        raise FaError(st, "fa_fwd_ex")
     return out, lse

@@ -79,17 +79,40 @@ __device__ __forceinline__ i16x4 ds_read_tr16(const short* lds_ptr) {
       (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) short*)lds_ptr));
 }
 
+// One launch: B batches of Hq query heads; query head h reads K/V head h / group.
+// Tensors are [B, heads, rows, d] with arbitrary batch/head/row strides (elements)
+// and contiguous d; LSE is [B, Hq, Nq] contiguous.
 struct Params {
   const short* q;
   const short* k;
   const short* v;
   short* o;
   float* lse;
-  int N;
-  int num_m_blocks;   // ceil(N / BM)
-  int total_wgs;      // B * H * num_m_blocks
+  int Nq, Nk;         // query rows, key rows per slice
+  int Hq;             // query heads
+  int group;          // query heads per K/V head
+  int causal_off;     // causal: key j is valid for query i iff j <= i + causal_off
+  int q_sr, k_sr, v_sr, o_sr;                      // row strides
+  int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;   // batch and head strides
+  uint32_t q_bytes, k_bytes, v_bytes;              // extent of one slice: rows past it read as zeros
+  int num_m_blocks;   // ceil(Nq / BM)
+  int total_wgs;      // B * Hq * num_m_blocks
   float c;            // scale * log2(e)
 };
+
+// Base pointers of one (batch, query head) slice and of the K/V head it reads.
+struct Slice {
+  const short* q;
+  const short* k;
+  const short* v;
+  short* o;
+};
+__device__ __forceinline__ Slice slice_of(const Params& p, int bh) {
+  const int b = bh / p.Hq, h = bh - b * p.Hq, kh = h / p.group;
+  return {p.q + b * p.q_sb + h * p.q_sh, p.k + b * p.k_sb + kh * p.k_sh, p.v + b * p.v_sb + kh * p.v_sh,
+          p.o + b * p.o_sb + h * p.o_sh};
+}
+
 
 // The softmax keeps its exponent reference while a lane's weights of one tile sum to
 // at most this, which bounds every weight by it as well (2^8, far inside fp16's
@@ -182,13 +205,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   const int bh = w / p.num_m_blocks;
   int mb = w - bh * p.num_m_blocks;
   if (CAUSAL) mb = p.num_m_blocks - 1 - mb;   // longest rows first
-  const int N = p.N;
+  const int Nq = p.Nq, Nk = p.Nk, off = p.causal_off;
   const int m0 = mb * BM;
-  const int64_t head = (int64_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;   // < 2^32: the host checks N*d < 2^31
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head, head_bytes);
+  const Slice sl = slice_of(p, bh);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(sl.q, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(sl.k, p.k_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(sl.v, p.v_bytes);
 
   const int tid = threadIdx.x;
   // the wave index is uniform across the wave; saying so keeps LDS-load bases and
@@ -220,32 +242,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   // Direct-to-LDS loads: load i of a tile fills LDS bytes [1024 i, 1024 i + 1024),
   // i.e. rows ROWS_PER_DMA*i.. of the tile; lane l fills tile row
   // ROWS_PER_DMA*i + 16 l / (2D), chunk position p = (16 l mod 2D) / 16, and so fetches
-  // source chunk p ^ swz(row). This wave issues loads i = NW kk + wave.
-  uint32_t dma_off[DMA_PER_WAVE];
+  // source chunk p ^ swz(row). This wave issues loads i = NW kk + wave. K and V
+  // may have different row strides, so each has its own lane offsets.
+  uint32_t dma_off_k[DMA_PER_WAVE], dma_off_v[DMA_PER_WAVE];
 #pragma unroll
   for (int kk = 0; kk < DMA_PER_WAVE; ++kk) {
     const int i = kk * NW + wave;
     const int r_local = (16 * lane) / (2 * D);
     const int pch = ((16 * lane) % (2 * D)) / 16;
     const int r = ROWS_PER_DMA * (i % PATS) + r_local;               // tile row mod 16
-    dma_off[kk] = (uint32_t)((r_local * D + ((pch ^ swz<D>(r)) << 3)) * 2);
+    const int col = (pch ^ swz<D>(r)) << 3;
+    dma_off_k[kk] = (uint32_t)((r_local * p.k_sr + col) * 2);
+    dma_off_v[kk] = (uint32_t)((r_local * p.v_sr + col) * 2);
   }
-  auto issue_tile_load = [&](const __amdgpu_buffer_rsrc_t& rsrc, short* dst, int n0) {
+  auto issue_tile_load = [&](const __amdgpu_buffer_rsrc_t& rsrc, const uint32_t (&lane_off)[DMA_PER_WAVE], int sr,
+                             short* dst, int n0) {
 #pragma unroll
     for (int kk = 0; kk < DMA_PER_WAVE; ++kk) {
       const int i = kk * NW + wave;
-      buffer_load16_to_lds(rsrc, dst + 512 * i, dma_off[kk], (uint32_t)((n0 * D + 512 * i) * 2));
+      buffer_load16_to_lds(rsrc, dst + 512 * i, lane_off[kk], (uint32_t)((n0 + ROWS_PER_DMA * i) * sr * 2));
     }
   };
 
   // ---- Q^T as the B operand, kept in registers for the whole loop ----
-  // qf[qb][ks] = Q[wq0 + 32 qb + l32][16 ks + 8 hi .. +7] (zeros past N).
+  // qf[qb][ks] = Q[wq0 + 32 qb + l32][16 ks + 8 hi .. +7] (zeros past Nq).
   i16x8 qf[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-      qf[qb][ks] = buffer_load16(rq, (uint32_t)(((wq0 + 32 * qb + l32) * D + ks * 16 + 8 * hi) * 2));
+      qf[qb][ks] = buffer_load16(rq, (uint32_t)(((wq0 + 32 * qb + l32) * p.q_sr + ks * 16 + 8 * hi) * 2));
 
   f32x16 acc_o[QB][D / 32];
 #pragma unroll
@@ -264,10 +290,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   i16x8 pprev[QB][BN / 16];   // P of the previous tile as 16-bit B operands
 
   // Tiles [0, n_full) need no mask for any query of this workgroup; the rest
-  // (the causal diagonal band and the ragged last tile) do.
-  const int n_end = CAUSAL ? min(N, m0 + BM) : N;
+  // (the causal diagonal band and the ragged last tile) do. Under a causal mask the
+  // workgroup's last query sees keys up to m0 + BM - 1 + off; none may be visible.
+  const int n_end = CAUSAL ? max(0, min(Nk, m0 + BM + off)) : Nk;
   const int ntiles = (n_end + BN - 1) / BN;
-  int n_full = (CAUSAL ? min(N, m0 + 1) : N) / BN;   // keys < n_full*BN are valid for every query
+  int n_full = (CAUSAL ? max(0, min(Nk, m0 + 1 + off)) : Nk) / BN;   // keys < n_full*BN: valid for every query
   if (n_full > ntiles) n_full = ntiles;
 
   auto pv = [&](const short* vbuf) {
@@ -321,7 +348,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= N || (CAUSAL && key > query)) s[qb][kb][r] = -INFINITY;
+            if (key >= Nk || (CAUSAL && key > query + off)) s[qb][kb][r] = -INFINITY;
           }
       }
     }
@@ -368,7 +395,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
         const float cand = max_halves(mx) * c;
         const float ref_new = cand > ref[qb] ? cand : ref[qb];
-        const float alpha = __builtin_amdgcn_exp2f(ref[qb] - ref_new);   // 1 exactly if unmoved, 0 from -inf
+        // 1 if the reference did not move (also while it is still -inf: a row with no
+        // visible key so far), 0 when it leaves -inf
+        const float alpha = (ref_new == ref[qb]) ? 1.f : __builtin_amdgcn_exp2f(ref[qb] - ref_new);
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -395,12 +424,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   auto full_tile = [&](int j, short* k_rd, short* k_wr, short* v_rd, short* v_wr, auto prev_tag) {
     const int n0 = j * BN;
     sync_tile();
-    if (j + 1 < ntiles) issue_tile_load(rk, k_wr, n0 + BN);
-    issue_tile_load(rv, v_wr, n0);
+    if (j + 1 < ntiles) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
+    issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
     step(n0, k_rd, v_rd, std::false_type{}, prev_tag);
   };
   bool have_prev = false;   // pprev holds the weights of tile j-1 (wave-uniform)
-  if (ntiles > 0) issue_tile_load(rk, lds_k0, 0);
+  if (ntiles > 0) issue_tile_load(rk, dma_off_k, p.k_sr, lds_k0, 0);
   int j = 0;
   if (n_full > 0) {
     full_tile(0, lds_k0, lds_k1, lds_v1, lds_v0, std::false_type{});
@@ -422,9 +451,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     short* v_rd = (j & 1) ? lds_v0 : lds_v1;
     short* v_wr = (j & 1) ? lds_v1 : lds_v0;
     sync_tile();
-    if (j + 1 < ntiles) issue_tile_load(rk, k_wr, n0 + BN);
-    issue_tile_load(rv, v_wr, n0);
-    if (CAUSAL && n0 > wq0 + 32 * QB - 1) {   // whole tile in this wave's future
+    if (j + 1 < ntiles) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
+    issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
+    if (CAUSAL && n0 > wq0 + 32 * QB - 1 + off) {   // whole tile in this wave's future
       if (have_prev) pv(v_rd);
       have_prev = false;
       continue;
@@ -442,8 +471,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     const int qrow = wq0 + 32 * qb + l32;
     const float l_tot = sum_halves(l_run[qb]);
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    if (qrow < N) {
-      short* orow = p.o + head + (int64_t)qrow * D;
+    if (qrow < Nq) {
+      short* orow = sl.o + (int64_t)qrow * p.o_sr;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -457,7 +486,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
         }
       if (hi == 0) {
         const float lse = (l_tot > 0.f) ? kLn2 * (ref[qb] + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
-        p.lse[(int64_t)bh * N + qrow] = lse;
+        p.lse[(int64_t)bh * Nq + qrow] = lse;
       }
     }
   }
@@ -528,13 +557,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int bh = w / p.num_m_blocks;
   int mb = w - bh * p.num_m_blocks;
   if (CAUSAL) mb = p.num_m_blocks - 1 - mb;
-  const int N = p.N;
+  const int Nq = p.Nq, Nk = p.Nk, off = p.causal_off;
   const int m0 = mb * BM;
-  const int64_t head = (int64_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + head, head_bytes);
+  const Slice sl = slice_of(p, bh);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(sl.q, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(sl.k, p.k_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(sl.v, p.v_bytes);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -547,13 +575,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float c = p.c;
 
   // tiles the workgroup streams, tiles this wave computes, tiles it needs no mask for
-  const int n_end = CAUSAL ? min(N, m0 + BM) : N;
+  const int n_end = CAUSAL ? max(0, min(Nk, m0 + BM + off)) : Nk;
   const int T = (n_end + BN - 1) / BN;
   int Tw = 0, n_full = 0;
-  if (wq0 < N) {
-    const int w_end = CAUSAL ? min(N, wq0 + 32 * QB) : N;
+  if (wq0 < Nq) {
+    const int w_end = CAUSAL ? max(0, min(Nk, wq0 + 32 * QB + off)) : Nk;
     Tw = (w_end + BN - 1) / BN;
-    n_full = min(Tw, (CAUSAL ? min(N, wq0 + 1) : N) / BN);
+    n_full = min(Tw, (CAUSAL ? max(0, min(Nk, wq0 + 1 + off)) : Nk) / BN);
   }
 
   // ---- LDS fragment offsets (elements), as in fa_fwd_kernel ----
@@ -584,7 +612,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int r_local = (16 * lane) / (2 * D);
     const int pch = ((16 * lane) % (2 * D)) / 16;
     const int r = ROWS_PER_DMA * (ch % PATS) + r_local;
-    dma_off[t] = (uint32_t)((r_local * D + ((pch ^ swz<D>(r)) << 3)) * 2);
+    dma_off[t] = (uint32_t)((r_local * (dma_is_k[t] ? p.k_sr : p.v_sr) + ((pch ^ swz<D>(r)) << 3)) * 2);
   }
   // loads of K(jk) into kdst (if has_k) and V(jv) into vdst (if has_v); wave-uniform flags
   auto issue_loads = [&](short* kdst, short* vdst, int jk, int jv, bool has_k, bool has_v) __attribute__((always_inline)) {
@@ -592,10 +620,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int t = 0; t < LOADS_PER_WAVE; ++t) {
       if (dma_is_k[t]) {
         if (has_k)
-          buffer_load16_to_lds(rk, kdst + 512 * dma_chunk[t], dma_off[t], (uint32_t)((jk * BN * D + 512 * dma_chunk[t]) * 2));
+          buffer_load16_to_lds(rk, kdst + 512 * dma_chunk[t], dma_off[t],
+                               (uint32_t)((jk * BN + ROWS_PER_DMA * dma_chunk[t]) * p.k_sr * 2));
       } else {
         if (has_v)
-          buffer_load16_to_lds(rv, vdst + 512 * dma_chunk[t], dma_off[t], (uint32_t)((jv * BN * D + 512 * dma_chunk[t]) * 2));
+          buffer_load16_to_lds(rv, vdst + 512 * dma_chunk[t], dma_off[t],
+                               (uint32_t)((jv * BN + ROWS_PER_DMA * dma_chunk[t]) * p.v_sr * 2));
       }
     }
   };
@@ -615,7 +645,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      qf[qb][ks] = buffer_load16(rq, (uint32_t)(((wq0 + 32 * qb + l32) * D + ks * 16 + 8 * hi) * 2));
+      qf[qb][ks] = buffer_load16(rq, (uint32_t)(((wq0 + 32 * qb + l32) * p.q_sr + ks * 16 + 8 * hi) * 2));
   f32x16 acc_o[QB][NDB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
@@ -713,7 +743,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= N || (CAUSAL && key > query)) s[qb][kb][r] = -INFINITY;
+            if (key >= Nk || (CAUSAL && key > query + off)) s[qb][kb][r] = -INFINITY;
           }
       }
     }
@@ -732,7 +762,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
         const float cand = max_halves(mx) * c;             // fl(c * row max), -inf if none valid
         const float ref_new = cand > ref[qb] ? cand : ref[qb];
-        const float alpha = __builtin_amdgcn_exp2f(ref[qb] - ref_new);   // 1 exactly if unmoved, 0 from -inf
+        // 1 if the reference did not move (also while it is still -inf: a row with no
+        // visible key so far), 0 when it leaves -inf
+        const float alpha = (ref_new == ref[qb]) ? 1.f : __builtin_amdgcn_exp2f(ref[qb] - ref_new);
         l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -822,8 +854,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int qrow = wq0 + 32 * qb + l32;
     const float l_tot = sum_halves(l_run[qb]);
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    if (qrow < N) {
-      short* orow = p.o + head + (int64_t)qrow * D;
+    if (qrow < Nq) {
+      short* orow = sl.o + (int64_t)qrow * p.o_sr;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -836,7 +868,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       if (hi == 0) {
         const float lse = (l_tot > 0.f) ? kLn2 * (ref[qb] + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
-        p.lse[(int64_t)bh * N + qrow] = lse;
+        p.lse[(int64_t)bh * Nq + qrow] = lse;
       }
     }
   }
@@ -895,39 +927,73 @@ bool tile_ok(int64_t d, int bm, int bn) {
   return false;
 }
 
-fa_status validate(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                   int64_t H, int64_t N, int64_t d, float scale, fa_dtype dtype) {
-  if (B < 0 || H < 0 || N < 0) return FA_ERR_BAD_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
-  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_BAD_SCALE;
-  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_BAD_DTYPE;
-  if (B == 0 || H == 0 || N == 0) return FA_OK;
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_MISALIGNED;
-  if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
-  // N*d < 2^31 elements: per-head byte offsets (and buffer ranges) fit 32 bits
-  if (N >= ((int64_t)1 << 31) / d) return FA_ERR_TOO_LARGE;
+// Row r of a slice with row stride sr is addressed as (r * sr + column) * 2 bytes in
+// 32-bit arithmetic, for rows up to N + 512 (the padded last block).
+bool rows_fit(int64_t N, int64_t sr) { return (N + 512) * sr < ((int64_t)1 << 30); }
+
+// strides: {batch, head, row} in elements, non-negative multiples of 8 (16 bytes),
+// row stride >= d; nullptr means contiguous [B, H, N, d].
+fa_status read_strides(const int64_t* st, int64_t H, int64_t N, int64_t d, int64_t out[3]) {
+  if (!st) {
+    out[0] = H * N * d;
+    out[1] = N * d;
+    out[2] = d;
+    return FA_OK;
+  }
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0 || (st[i] & 7)) return FA_ERR_BAD_STRIDE;
+    out[i] = st[i];
+  }
+  if (out[2] < d) return FA_ERR_BAD_STRIDE;
   return FA_OK;
 }
 
-fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-              int64_t N, int64_t d, float scale, int causal, fa_dtype dtype, void* stream, int bm, int bn) {
-  fa_status st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype);
-  if (st != FA_OK) return st;
+fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+              int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, const int64_t* qs_in, const int64_t* ks_in,
+              const int64_t* vs_in, const int64_t* os_in, float scale, int causal, fa_dtype dtype,
+              void* stream, int bm, int bn) {
+  if (B < 0 || Hq < 0 || Hk < 0 || Nq < 0 || Nk < 0) return FA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_BAD_DTYPE;
   if (!tile_ok(d, bm, bn)) return FA_ERR_UNSUPPORTED_TILE;
-  if (B == 0 || H == 0 || N == 0) return FA_OK;
-  const int64_t mblocks = (N + bm - 1) / bm;
-  if (B >= ((int64_t)1 << 31) || H >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
-  if (B * H >= ((int64_t)1 << 31) / mblocks + 1) return FA_ERR_TOO_LARGE;
+  if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
+  if (Hk == 0 || Hq % Hk != 0) return FA_ERR_BAD_SHAPE;
+  if (!q || !o || !lse) return FA_ERR_NULL_PTR;
+  if (Nk > 0 && (!k || !v)) return FA_ERR_NULL_PTR;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  fa_status st;
+  if ((st = read_strides(qs_in, Hq, Nq, d, qs)) != FA_OK) return st;
+  if ((st = read_strides(ks_in, Hk, Nk, d, ks)) != FA_OK) return st;
+  if ((st = read_strides(vs_in, Hk, Nk, d, vs)) != FA_OK) return st;
+  if ((st = read_strides(os_in, Hq, Nq, d, os)) != FA_OK) return st;
+  if (!rows_fit(Nq, qs[2]) || !rows_fit(Nq, os[2]) || !rows_fit(Nk, ks[2]) || !rows_fit(Nk, vs[2]))
+    return FA_ERR_TOO_LARGE;
+  const int64_t mblocks = (Nq + bm - 1) / bm;
+  if (B >= ((int64_t)1 << 31) || Hq >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
+  if (B * Hq >= ((int64_t)1 << 31) / mblocks + 1) return FA_ERR_TOO_LARGE;
+  const int64_t total = B * Hq * mblocks;
+  if (total >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
   Params p;
   p.q = (const short*)q;
   p.k = (const short*)k;
   p.v = (const short*)v;
   p.o = (short*)o;
   p.lse = lse;
-  p.N = (int)N;
-  const int64_t total = B * H * mblocks;
-  if (total >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.Hq = (int)Hq;
+  p.group = (int)(Hq / Hk);
+  p.causal_off = (int)(Nk - Nq);   // bottom-right alignment; 0 (top-left) when Nq = Nk
+  p.q_sb = qs[0]; p.q_sh = qs[1]; p.q_sr = (int)qs[2];
+  p.k_sb = ks[0]; p.k_sh = ks[1]; p.k_sr = (int)ks[2];
+  p.v_sb = vs[0]; p.v_sh = vs[1]; p.v_sr = (int)vs[2];
+  p.o_sb = os[0]; p.o_sh = os[1]; p.o_sr = (int)os[2];
+  p.q_bytes = (uint32_t)((Nq - 1) * qs[2] + d) * 2;
+  p.k_bytes = Nk > 0 ? (uint32_t)((Nk - 1) * ks[2] + d) * 2 : 0;
+  p.v_bytes = Nk > 0 ? (uint32_t)((Nk - 1) * vs[2] + d) * 2 : 0;
   p.num_m_blocks = (int)mblocks;
   p.total_wgs = (int)total;
   p.c = (float)((double)scale * 1.4426950408889634);  // s * log2(e), rounded once
@@ -967,13 +1033,24 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  void* stream) {
   int bm, bn;
   default_tile(N, d, causal, &bm, &bn);
-  return run(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream, bm, bn);
+  return run(q, k, v, o, lse, B, H, H, N, N, d, nullptr, nullptr, nullptr, nullptr, scale, causal, dtype,
+             stream, bm, bn);
 }
 
 fa_status fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                        int64_t H, int64_t N, int64_t d, float scale, int causal, fa_dtype dtype,
                        void* stream, int block_m, int block_n) {
-  return run(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream, block_m, block_n);
+  return run(q, k, v, o, lse, B, H, H, N, N, d, nullptr, nullptr, nullptr, nullptr, scale, causal, dtype,
+             stream, block_m, block_n);
+}
+
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                    int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, const int64_t* q_strides,
+                    const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
+                    float scale, int causal, fa_dtype dtype, void* stream, int block_m, int block_n) {
+  if (block_m == 0 && block_n == 0) default_tile(Nq, d, causal, &block_m, &block_n);
+  return run(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, q_strides, k_strides, v_strides, o_strides, scale,
+             causal, dtype, stream, block_m, block_n);
 }
 
 int fa_tile_supported(int64_t d, int block_m, int block_n) { return tile_ok(d, block_m, block_n) ? 1 : 0; }
@@ -991,14 +1068,15 @@ const char* fa_status_str(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL_PTR: return "null pointer";
-    case FA_ERR_BAD_SHAPE: return "negative B, H or N";
+    case FA_ERR_BAD_SHAPE: return "negative size, or Hq not a positive multiple of Hk";
     case FA_ERR_UNSUPPORTED_HEADDIM: return "head dimension must be 64 or 128";
     case FA_ERR_BAD_SCALE: return "scale must be finite and > 0";
     case FA_ERR_BAD_DTYPE: return "dtype must be FA_F16 or FA_BF16";
     case FA_ERR_MISALIGNED: return "q/k/v/o must be 16-byte aligned and lse 4-byte aligned";
-    case FA_ERR_TOO_LARGE: return "problem too large (N*d >= 2^31 or grid >= 2^31)";
+    case FA_ERR_TOO_LARGE: return "problem too large ((N + 512) * row stride >= 2^30 or grid >= 2^31)";
     case FA_ERR_UNSUPPORTED_TILE: return "tile shape not compiled";
     case FA_ERR_HIP: return "HIP launch error";
+    case FA_ERR_BAD_STRIDE: return "strides must be non-negative multiples of 8 elements, row stride >= d";
     default: return "unknown status";
   }
 }

@@ -37,14 +37,15 @@ typedef enum {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL_PTR = 1,           /* a required pointer is NULL */
-  FA_ERR_BAD_SHAPE = 2,          /* B, H or N negative */
+  FA_ERR_BAD_SHAPE = 2,          /* a size is negative, or Hq is not a positive multiple of Hk */
   FA_ERR_UNSUPPORTED_HEADDIM = 3,/* d is not 64 or 128 */
   FA_ERR_BAD_SCALE = 4,          /* scale is not finite or not > 0 */
   FA_ERR_BAD_DTYPE = 5,          /* dtype is not FA_F16 / FA_BF16 */
   FA_ERR_MISALIGNED = 6,         /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
-  FA_ERR_TOO_LARGE = 7,          /* N*d >= 2^31 elements, or the grid exceeds 2^31-1 workgroups */
+  FA_ERR_TOO_LARGE = 7,          /* (N + 512) * row stride >= 2^30 elements, or the grid exceeds 2^31-1 workgroups */
   FA_ERR_UNSUPPORTED_TILE = 8,   /* (block_m, block_n) not among the compiled tile shapes */
-  FA_ERR_HIP = 9                 /* the HIP runtime reported an error at launch */
+  FA_ERR_HIP = 9,                /* the HIP runtime reported an error at launch */
+  FA_ERR_BAD_STRIDE = 10         /* a stride is negative or not a multiple of 8 elements, or a row stride < d */
 } fa_status;
 
 /*
@@ -87,6 +88,37 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 fa_status fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
                        int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
                        fa_dtype dtype, void* stream, int block_m, int block_n);
+
+/*
+ * fa_fwd_ex — the general form of fa_fwd, asynchronous on `stream`: unequal query and
+ * key lengths, grouped K/V heads and strided tensors.
+ *
+ *   q, o    : [B, Hq, Nq, d] of `dtype`; o fully overwritten.
+ *   k, v    : [B, Hk, Nk, d] of `dtype`. Query head h reads K/V head h / (Hq / Hk)
+ *             (Hq must be a positive multiple of Hk: Hk = Hq is plain multi-head
+ *             attention, Hk = 1 shares one K/V head among all query heads).
+ *   lse     : [B, Hq, Nq] contiguous float32, fully overwritten.
+ *   *_strides: {batch, head, row} element strides of that tensor, d contiguous; NULL
+ *             means contiguous. Each stride is a non-negative multiple of 8 elements
+ *             (rows stay 16-byte aligned) and the row stride is at least d. K and V
+ *             may share storage or broadcast (stride 0); the rows of o must not
+ *             overlap each other or q, k, v.
+ *   causal  : nonzero masks key j > i + Nk - Nq for query i, the bottom-right
+ *             alignment ("用 CuTe 读懂 FlashAttention", causal section, names it as
+ *             the one that differs from top-left only when the lengths differ): the
+ *             last query sees every key. With Nq = Nk this is fa_fwd's mask. A query
+ *             with no visible key (Nq > Nk, i < Nq - Nk) gets O = 0 and LSE = -inf.
+ *   block_m, block_n: a compiled tile, or 0, 0 for the tile fa_fwd would choose for Nq.
+ *   Other arguments, ownership and errors as for fa_fwd; additionally
+ *   FA_ERR_BAD_STRIDE. Nk = 0 is allowed (every row gets O = 0, LSE = -inf; k and v
+ *   may then be NULL). B*Hq*Nq == 0 is a no-op.
+ */
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d,
+                    const int64_t* q_strides, const int64_t* k_strides,
+                    const int64_t* v_strides, const int64_t* o_strides,
+                    float scale, int causal, fa_dtype dtype, void* stream,
+                    int block_m, int block_n);
 
 /* 1 if (block_m, block_n) is compiled for head dimension d, else 0. */
 int fa_tile_supported(int64_t d, int block_m, int block_n);

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(10):
+    for code in range(11):
         s = fa.status_str(code)
         assert s and s != "unknown status"
     assert fa.status_str(99) == "unknown status"
@@ -71,6 +71,24 @@ def test_validation_codes_without_gpu():
     assert call(N=1 << 25) == 7                       # N*d >= 2^31 with d = 64
     assert call(B=1 << 20, H=1 << 20, N=1 << 10) == 7  # grid too large
     assert fa.fa_fwd_tiled(A, A, A, A, A, 1, 1, 64, 64, 0.1, 0, 0, None, 96, 64) == 8
+
+
+def call_ex(q=A, k=A, v=A, o=A, lse=A, B=1, Hq=4, Hk=2, Nq=64, Nk=100, d=64, qs=None, ks=None, vs=None,
+            os_=None, causal=0, bm=0, bn=0):
+    return fa.fa_fwd_ex(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, qs, ks, vs, os_, 0.125, causal, 0, None, bm, bn)
+
+
+def test_general_entry_validation_without_gpu():
+    assert call_ex(Hk=3) == 2 and call_ex(Hk=0) == 2 and call_ex(Nk=-1) == 2
+    assert call_ex(qs=(0, 0, 60)) == 10              # row stride < d
+    assert call_ex(ks=(8, 8, 68)) == 10              # not a multiple of 8
+    assert call_ex(vs=(-64, 64, 64)) == 10           # negative
+    assert call_ex(os_=(0, 64, 64), q=None) == 1     # null checked first
+    assert call_ex(k=None) == 1                      # Nk > 0 needs k and v
+    assert call_ex(qs=(0, 0, 1 << 24), Nq=100) == 7  # rows exceed 32-bit offsets
+    assert call_ex(bm=96, bn=64) == 8
+    assert call_ex(q=None, k=None, v=None, o=None, lse=None, Nq=0) == 0
+    assert call_ex(q=None, k=None, v=None, o=None, lse=None, Hq=0, Hk=0) == 0
 
 
 def test_empty_problems_need_no_pointers():

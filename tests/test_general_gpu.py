@@ -1,0 +1,178 @@
+"""GPU parity of the general entry point (fa_fwd_ex, through the C ABI) against the
+fp64 CPU oracle: strided layouts, grouped K/V heads, unequal query and key lengths
+with the bottom-right causal mask, and no keys at all.
+
+Tolerances as in test_parity_gpu.py (max |dO| <= 2e-3 fp16, <= 1e-2 bf16, max
+|dLSE| <= 1e-3), against the oracle on the very 16-bit inputs the GPU received.
+Grouped heads are checked against the oracle on K/V with each head repeated for
+its query heads (the definition of the grouping). Rows without a visible key must
+be exactly O = 0, LSE = -inf on both sides.
+
+V is drawn from N(0, 0.5^2): under a causal mask the first rows average a few V
+rows, and with N(0, 1) values |O| reaches 4, where bf16's own rounding of O and of
+the weights alone (half an ulp each, 2^-8 relative) can exceed the 1e-2 bound.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_forward_fwd_amd as fa
+import oracle
+from golden_io import load_worked_example
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"f16": 2e-3, "bf16": 1e-2}
+TOL_LSE = 1e-3
+TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+TILES = [None, (64, 64), (128, 32), (128, 64), (256, 32), (512, 32)]
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load_library()
+    yield
+
+
+def _rand(shape, dtype, seed, std=1.0):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return (torch.randn(shape, generator=g) * std).to(TORCH_DT[dtype])
+
+
+def _as_layout(t, layout):
+    """A GPU copy of [B, H, N, d] t in the given memory layout, returned as a
+    [B, H, N, d] view: 'bhnd' contiguous, 'bnhd' (heads interleaved per row), or
+    'padded' (rows 8 elements wider than d)."""
+    dev = torch.device("cuda:0")
+    if layout == "bhnd":
+        return t.to(dev).contiguous()
+    if layout == "bnhd":
+        return t.transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+    if layout == "padded":
+        B, H, N, d = t.shape
+        buf = torch.zeros((B, H, N, d + 8), dtype=t.dtype)
+        buf[..., :d] = t
+        return buf.to(dev)[..., :d]
+    raise ValueError(layout)
+
+
+def check(q, k, v, scale, causal, dtype, tile=None, layouts=("bhnd",) * 4, label=""):
+    """q [B,Hq,Nq,d], k/v [B,Hk,Nk,d] on the CPU in `dtype`; runs fa_fwd_ex and compares."""
+    B, Hq, Nq, d = q.shape
+    Hk = k.shape[1]
+    _say(f"[general] {label} q={tuple(q.shape)} k={tuple(k.shape)} {dtype} causal={causal} tile={tile} "
+         f"layouts={layouts}")
+    qd, kd, vd = _as_layout(q, layouts[0]), _as_layout(k, layouts[1]), _as_layout(v, layouts[2])
+    out = _as_layout(torch.full(q.shape, float("nan"), dtype=q.dtype), layouts[3])
+    lse = torch.full((B, Hq, Nq), float("nan"), dtype=torch.float32, device=qd.device)
+    bm, bn = tile if tile else (None, None)
+    fa.fwd_ex(qd, kd, vd, scale=scale, causal=causal, block_m=bm, block_n=bn, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_g = out.float().cpu().double().numpy()
+    l_g = lse.cpu().double().numpy()
+    g = Hq // Hk
+    k_rep = k.repeat_interleave(g, dim=1)
+    v_rep = v.repeat_interleave(g, dim=1)
+    o_ref, l_ref = oracle.attention_fwd(q.double().numpy(), k_rep.double().numpy(), v_rep.double().numpy(),
+                                        scale, causal, align="bottom-right")
+    empty = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(l_g), empty), "rows without a visible key differ"
+    assert np.all(o_g[empty] == 0.0), "rows without a visible key must give O = 0"
+    err_o = np.abs(o_g - o_ref).max() if o_g.size else 0.0
+    err_l = np.abs(l_g[~empty] - l_ref[~empty]).max() if (~empty).any() else 0.0
+    _say(f"[general]   max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} rows without keys={int(empty.sum())}")
+    assert err_o <= TOL_O[dtype], f"{label}: max|dO| = {err_o}"
+    assert err_l <= TOL_LSE, f"{label}: max|dLSE| = {err_l}"
+
+
+def _qkv(hq, hk, nq, nk, d, dtype, seed):
+    return (_rand((2, hq, nq, d), dtype, seed), _rand((2, hk, nk, d), dtype, seed + 1),
+            _rand((2, hk, nk, d), dtype, seed + 2, std=0.5))
+
+
+@pytest.mark.parametrize("layouts", [("bnhd",) * 4, ("padded", "bnhd", "padded", "bhnd"),
+                                     ("bhnd", "padded", "bnhd", "bnhd")], ids=["bnhd", "mixed1", "mixed2"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("tile", [None, (128, 32), (256, 32)])
+def test_strided_layouts(layouts, d, tile):
+    for dtype in ("f16", "bf16"):
+        q, k, v = _qkv(3, 3, 300, 300, d, dtype, seed=d + 7)
+        for causal in (False, True):
+            check(q, k, v, 1 / math.sqrt(d), causal, dtype, tile=tile, layouts=layouts, label="strides")
+
+
+@pytest.mark.parametrize("hq,hk", [(8, 2), (4, 1), (6, 3)])
+@pytest.mark.parametrize("tile", TILES)
+def test_grouped_kv_heads(hq, hk, tile):
+    for d in (64, 128):
+        if tile and not fa.fa_tile_supported(d, *tile):
+            continue
+        for dtype in ("f16", "bf16"):
+            q, k, v = _qkv(hq, hk, 200, 200, d, dtype, seed=hq * 10 + hk + d)
+            for causal in (False, True):
+                check(q, k, v, 1 / math.sqrt(d), causal, dtype, tile=tile, label=f"gqa {hq}/{hk}")
+
+
+@pytest.mark.parametrize("nq,nk", [(1, 1000), (5, 4096), (37, 515), (300, 100), (512, 77), (100, 100),
+                                   (1000, 1), (64, 4096)])
+@pytest.mark.parametrize("tile", TILES)
+def test_unequal_lengths(nq, nk, tile):
+    for d in (64, 128):
+        if tile and not fa.fa_tile_supported(d, *tile):
+            continue
+        dtype = "f16" if d == 64 else "bf16"
+        q, k, v = _qkv(2, 2, nq, nk, d, dtype, seed=nq + 3 * nk + d)
+        for causal in (False, True):
+            check(q, k, v, 1 / math.sqrt(d), causal, dtype, tile=tile, label=f"Nq={nq} Nk={nk}")
+
+
+def test_no_keys():
+    for d in (64, 128):
+        q = _rand((1, 2, 70, d), "f16", seed=1)
+        k = torch.zeros((1, 2, 0, d), dtype=torch.float16)
+        check(q, k, k.clone(), 0.1, False, "f16", label="Nk=0")
+        check(q, k, k.clone(), 0.1, True, "f16", label="Nk=0 causal")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("tile", TILES)
+def test_worked_example_bottom_right(dtype, tile):
+    """The blog's example keeps its two queries and four keys; bottom-right causal
+    gives the hand-derived values stored in the fixture (row 0 sees keys 0..2)."""
+    g = load_worked_example()
+    d = 64
+    Q = torch.zeros(1, 1, 2, d); K = torch.zeros(1, 1, 4, d); V = torch.zeros(1, 1, 4, d)
+    Q[0, 0, :, :2] = torch.tensor(g["Q"]); K[0, 0, :, :2] = torch.tensor(g["K"])
+    V[0, 0, :, :2] = torch.tensor(g["V"])
+    dt = TORCH_DT[dtype]
+    dev = torch.device("cuda:0")
+    bm, bn = tile if tile else (None, None)
+    for causal, exp_o, exp_l in ((True, g["bottom_right"]["O"], g["bottom_right"]["LSE"]), (False, g["O"], g["LSE"])):
+        o, lse = fa.fwd_ex(Q.to(dt).to(dev), K.to(dt).to(dev), V.to(dt).to(dev), scale=math.log(2.0),
+                           causal=causal, block_m=bm, block_n=bn)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(o.float().cpu().numpy()[0, 0, :, :2], exp_o, rtol=0, atol=TOL_O[dtype])
+        np.testing.assert_allclose(lse.cpu().numpy()[0, 0], exp_l, rtol=0, atol=TOL_LSE)
+
+
+def test_equal_lengths_match_fa_fwd_bitwise():
+    """With Nq = Nk, contiguous tensors and Hk = Hq the general entry point is fa_fwd."""
+    for d, dtype in ((64, "f16"), (128, "bf16")):
+        q, k, v = _qkv(4, 4, 515, 515, d, dtype, seed=5)
+        dev = torch.device("cuda:0")
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        for causal in (False, True):
+            o1, l1 = fa.fwd(qd, kd, vd, scale=0.1, causal=causal)
+            o2, l2 = fa.fwd_ex(qd, kd, vd, scale=0.1, causal=causal)
+            torch.cuda.synchronize()
+            assert torch.equal(o1, o2) and torch.equal(l1, l2)
