@@ -96,10 +96,14 @@ fa_status fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, flo
  *   q, o    : [B, Hq, Nq, d] of `dtype`; o fully overwritten.
  *   k, v    : [B, Hk, Nk, d] of `dtype`. Query head h reads K/V head h / (Hq / Hk)
  *             (Hq must be a positive multiple of Hk: Hk = Hq is plain multi-head
- *             attention, Hk = 1 shares one K/V head among all query heads).
+ *             attention, Hk = 1 shares one K/V head among all query heads). This is
+ *             the grouping of "CUDA 算子工程：手写 FlashAttention v2 之路" ch. 14,
+ *             §14.7.1 (one K/V head serving the query heads of its group), with
+ *             consecutive query heads forming a group.
  *   lse     : [B, Hq, Nq] contiguous float32, fully overwritten.
  *   *_strides: {batch, head, row} element strides of that tensor, d contiguous; NULL
- *             means contiguous. Each stride is a non-negative multiple of 8 elements
+ *             means contiguous (the arbitrary strides that "用 CuTe 读懂 FlashAttention"
+ *             lists among its tutorial's limitations). Each stride is a non-negative multiple of 8 elements
  *             (rows stay 16-byte aligned) and the row stride is at least d. K and V
  *             may share storage or broadcast (stride 0); the rows of o must not
  *             overlap each other or q, k, v.
