@@ -180,6 +180,63 @@ def time_workload(w, steps, warmup):
                 inputs=(q, k, v))
 
 
+def time_split(w, steps, warmup):
+    """Per-call device time of fa_fwd_split (attention launch + merge launch) at the
+    library's suggested split count, and of the unsplit fa_fwd_ex, on the same inputs."""
+    import torch
+    import exact_attention_forward_fwd_amd as fa
+    from exact_attention_forward_fwd_amd.workloads import make_general_inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in make_general_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device=dev)
+    dt = fa.FA_F16 if w.dtype == "f16" else fa.FA_BF16
+    splits = fa.fa_split_default(w.B, w.Hq, w.Hk, w.Nq, w.Nk, w.d, w.causal)
+    ws_bytes = fa.fa_split_workspace_bytes(w.B, w.Hq, w.Nq, w.d, splits)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    lib = fa.load_library()
+    st = [fa._binding._strides(t.stride()[:3]) for t in (q, k, v, o)]
+    base = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq, w.Hk, w.Nq, w.Nk,
+            w.d, *st, float(w.scale), int(w.causal), dt, sp, 0, 0)
+
+    def run(n_splits):
+        def call():
+            rc = lib.fa_fwd_split(*base, n_splits, ws.data_ptr(), ws.numel())
+            if rc != 0:
+                raise fa.FaError(rc, "fa_fwd_split")
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            call()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) for a, b in ev)
+        return sum(per) / len(per), per[len(per) // 2]
+
+    avg, med = run(splits)
+    avg1, _ = run(1)
+    rec = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+           "dtype": w.dtype, "causal": w.causal, "splits": splits,
+           "call_ms_avg": round(avg, 5), "call_ms_median": round(med, 5),
+           "unsplit_ms_avg": round(avg1, 5), "speedup_vs_unsplit": round(avg1 / avg, 2)}
+    if w.flops / w.hbm_bytes < MFMA_PEAK_TFLOPS / (HBM_PEAK_GBS * 1e-3):
+        # below the ridge point (decoding): bounded by streaming K and V from HBM
+        gbs = w.hbm_bytes / (avg * 1e-3) / 1e9
+        rec["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": w.hbm_bytes}
+    else:
+        tf = w.flops / (avg * 1e-3) / 1e12
+        rec["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "algorithmic_flop": w.flops}
+    return rec
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The fp64 oracle on this workload's inputs: whole (b, h) slices, in order, until
     the budget is spent (at least one slice)."""
@@ -275,6 +332,10 @@ def main():
             del ro
             torch.cuda.empty_cache()
         out["other_workloads"] = others
+        from exact_attention_forward_fwd_amd.workloads import SPLIT_WORKLOADS
+        out["split_kv"] = [time_split(ws, max(10, args.steps // 2), max(3, args.warmup // 2))
+                           for ws in SPLIT_WORKLOADS.values()]
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)

@@ -18,9 +18,11 @@ FA_BF16 = 1
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED_HEADDIM",
     4: "FA_ERR_BAD_SCALE", 5: "FA_ERR_BAD_DTYPE", 6: "FA_ERR_MISALIGNED", 7: "FA_ERR_TOO_LARGE",
-    8: "FA_ERR_UNSUPPORTED_TILE", 9: "FA_ERR_HIP", 10: "FA_ERR_BAD_STRIDE",
+    8: "FA_ERR_UNSUPPORTED_TILE", 9: "FA_ERR_HIP", 10: "FA_ERR_BAD_STRIDE", 11: "FA_ERR_BAD_SPLITS",
+    12: "FA_ERR_WORKSPACE",
 }
-EXPORTED = ("fa_fwd", "fa_fwd_tiled", "fa_fwd_ex", "fa_tile_supported", "fa_default_tile", "fa_status_str")
+EXPORTED = ("fa_fwd", "fa_fwd_tiled", "fa_fwd_ex", "fa_fwd_split", "fa_split_workspace_bytes", "fa_split_default",
+            "fa_tile_supported", "fa_default_tile", "fa_status_str")
 
 
 class FaError(RuntimeError):
@@ -51,6 +53,13 @@ def load_library(path: str = LIB_PATH):
     lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p,
                               ctypes.c_float, i32, i32, vp, i32, i32]
     lib.fa_fwd_ex.restype = i32
+    lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p,
+                                 ctypes.c_float, i32, i32, vp, i32, i32, i32, vp, ctypes.c_size_t]
+    lib.fa_fwd_split.restype = i32
+    lib.fa_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    lib.fa_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_split_default.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, i32]
+    lib.fa_split_default.restype = i32
     lib.fa_tile_supported.argtypes = [i64, i32, i32]
     lib.fa_tile_supported.restype = i32
     lib.fa_default_tile.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -89,6 +98,24 @@ def fa_fwd_ex(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, q_strides, k_strides, v_str
     return load_library().fa_fwd_ex(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, _strides(q_strides),
                                     _strides(k_strides), _strides(v_strides), _strides(o_strides),
                                     scale, int(causal), dtype, stream, int(block_m), int(block_n))
+
+
+def fa_fwd_split(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, q_strides, k_strides, v_strides, o_strides,
+                 scale, causal, dtype, stream, block_m, block_n, num_splits, workspace, workspace_bytes) -> int:
+    """Raw C call of the split-KV entry point; workspace is a device address (or 0)."""
+    return load_library().fa_fwd_split(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, _strides(q_strides),
+                                       _strides(k_strides), _strides(v_strides), _strides(o_strides),
+                                       scale, int(causal), dtype, stream, int(block_m), int(block_n),
+                                       int(num_splits), workspace, int(workspace_bytes))
+
+
+def fa_split_workspace_bytes(B: int, Hq: int, Nq: int, d: int, num_splits: int) -> int:
+    return int(load_library().fa_split_workspace_bytes(B, Hq, Nq, d, int(num_splits)))
+
+
+def fa_split_default(B: int, Hq: int, Hk: int, Nq: int, Nk: int, d: int, causal: bool, block_m: int = 0,
+                     block_n: int = 0) -> int:
+    return int(load_library().fa_split_default(B, Hq, Hk, Nq, Nk, d, int(causal), int(block_m), int(block_n)))
 
 
 def fa_tile_supported(d: int, block_m: int, block_n: int) -> bool:
@@ -153,14 +180,8 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, block_m: int 
     return out, lse
 
 
-def fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, block_m: int | None = None,
-           block_n: int | None = None, out=None, lse=None, stream=None):
-    """General attention forward on torch tensors: q [B, Hq, Nq, d], k and v [B, Hk, Nk, d]
-    with any strides whose last dimension is contiguous; Hq a multiple of Hk (query
-    head h reads K/V head h // (Hq // Hk)). ``causal`` masks key j > i + Nk - Nq
-    (bottom-right alignment). Returns (o, lse): o [B, Hq, Nq, d] laid out like q
-    unless ``out`` is given, lse float32 [B, Hq, Nq] contiguous.
-    """
+def _general_args(q, k, v, scale, out, lse, stream):
+    """Checks and defaults shared by fwd_ex and fwd_split."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
@@ -174,8 +195,6 @@ def fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, block_m: i
     B, Hq, Nq, d = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
         raise ValueError("k and v must be [B, Hk, Nk, d] with q's B and d")
-    Hk, Nk = k.shape[1], k.shape[2]
-    dt = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -189,9 +208,51 @@ def fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, block_m: i
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return scale, out, lse, sp
+
+
+def fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, block_m: int | None = None,
+           block_n: int | None = None, out=None, lse=None, stream=None):
+    """General attention forward on torch tensors: q [B, Hq, Nq, d], k and v [B, Hk, Nk, d]
+    with any strides whose last dimension is contiguous; Hq a multiple of Hk (query
+    head h reads K/V head h // (Hq // Hk)). ``causal`` masks key j > i + Nk - Nq
+    (bottom-right alignment). Returns (o, lse): o [B, Hq, Nq, d] laid out like q
+    unless ``out`` is given, lse float32 [B, Hq, Nq] contiguous.
+    """
+    scale, out, lse, sp = _general_args(q, k, v, scale, out, lse, stream)
+    B, Hq, Nq, d = q.shape
+    Hk, Nk = k.shape[1], k.shape[2]
     st = fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hk,
                    Nq, Nk, d, q.stride()[:3], k.stride()[:3], v.stride()[:3], out.stride()[:3],
-                   float(scale), causal, dt, sp, block_m or 0, block_n or 0)
+                   float(scale), causal, _dtype_code(q), sp, block_m or 0, block_n or 0)
     if st != 0:
         raise FaError(st, "fa_fwd_ex")
+    return out, lse
+
+
+def fwd_split(q, k, v, scale: float | None = None, causal: bool = False, num_splits: int | None = None,
+              block_m: int | None = None, block_n: int | None = None, out=None, lse=None, workspace=None,
+              stream=None):
+    """fwd_ex with the keys of every query block divided among ``num_splits`` workgroups
+    (split-KV) and merged by a second kernel. ``num_splits`` defaults to the library's
+    suggestion (fa_split_default). ``workspace``: a device tensor of at least
+    fa_split_workspace_bytes(...) bytes; allocated here if None.
+    """
+    import torch
+    scale, out, lse, sp = _general_args(q, k, v, scale, out, lse, stream)
+    B, Hq, Nq, d = q.shape
+    Hk, Nk = k.shape[1], k.shape[2]
+    bm, bn = block_m or 0, block_n or 0
+    if num_splits is None:
+        num_splits = fa_split_default(B, Hq, Hk, Nq, Nk, d, causal, bm, bn)
+    need = fa_split_workspace_bytes(B, Hq, Nq, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hk,
+                      Nq, Nk, d, q.stride()[:3], k.stride()[:3], v.stride()[:3], out.stride()[:3],
+                      float(scale), causal, _dtype_code(q), sp, bm, bn, num_splits, ws_ptr, ws_bytes)
+    if st != 0:
+        raise FaError(st, "fa_fwd_split")
     return out, lse

@@ -96,9 +96,36 @@ struct Params {
   int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;   // batch and head strides
   uint32_t q_bytes, k_bytes, v_bytes;              // extent of one slice: rows past it read as zeros
   int num_m_blocks;   // ceil(Nq / BM)
-  int total_wgs;      // B * Hq * num_m_blocks
+  int num_splits;     // key ranges per query block (split-KV); 1: all keys in one workgroup
+  int split_keys;     // keys per range, a multiple of the key tile
+  int slices;         // B * Hq
+  int total_wgs;      // slices * num_splits * num_m_blocks
   float c;            // scale * log2(e)
+  // Split-KV partial results, or null: O_k = U_k / l_k as fp32 [num_splits][slices][Nq][d]
+  // and LSE_k as [num_splits][slices][Nq], in place of o and lse.
+  float* po;
+  float* plse;
 };
+
+// Work item of a workgroup: slice (batch, query head), key range and query block.
+// The workgroups of one XCD take a contiguous range of items (dispatch is
+// round-robin over the 8 XCDs), so the query blocks that stream the same K and V
+// share that XCD's L2. Under a causal mask the longest query blocks go first.
+struct WorkItem { int bh, split, mb; };
+template <bool CAUSAL>
+__device__ __forceinline__ WorkItem work_item(const Params& p) {
+  const int bid = blockIdx.x;
+  const int T = p.total_wgs;
+  const int xcd = bid & 7, slot = bid >> 3, per = T >> 3, rem = T & 7;
+  const int w = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int per_slice = p.num_m_blocks * p.num_splits;
+  const int bh = w / per_slice;
+  const int r = w - bh * per_slice;
+  const int split = r / p.num_m_blocks;
+  int mb = r - split * p.num_m_blocks;
+  if (CAUSAL) mb = p.num_m_blocks - 1 - mb;
+  return {bh, split, mb};
+}
 
 // Base pointers of one (batch, query head) slice and of the K/V head it reads.
 struct Slice {
@@ -153,6 +180,55 @@ __device__ __forceinline__ int swz(int r) {
   else return ((r & 3) << 2) | ((r >> 2) & 3);
 }
 
+// Epilogue of one wave: O = U / l and LSE = ln2 (ref + log2 l) for its QB blocks of 32
+// queries (l is split between the two lane halves), rounded into o and lse; or, for
+// a split-KV range, the fp32 partials O_k and LSE_k. A row with no visible key
+// (l = 0) gets O = 0 and LSE = -inf. acc_o[qb][db][4 g + e] of lane (hi, l32) holds
+// U^T[d = 32 db + 8 g + 4 hi + e][query wq0 + 32 qb + l32].
+template <int D, bool BF16, int QB>
+__device__ __forceinline__ void write_rows(const Params& p, const Slice& sl, int bh, int split, int wq0, int lane,
+                                           const f32x16 (&acc_o)[QB][D / 32], const float (&ref)[QB],
+                                           const float (&l_run)[QB]) {
+  using f32x2 = float __attribute__((ext_vector_type(2)));
+  using f32x4 = float __attribute__((ext_vector_type(4)));
+  using e16x2 = typename std::conditional<BF16, __bf16 __attribute__((ext_vector_type(2))),
+                                          _Float16 __attribute__((ext_vector_type(2)))>::type;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = wq0 + 32 * qb + l32;
+    const float l_tot = sum_halves(l_run[qb]);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    if (qrow >= p.Nq) continue;
+    const float lse = (l_tot > 0.f) ? kLn2 * (ref[qb] + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
+    if (p.po) {
+      const int64_t row = ((int64_t)split * p.slices + bh) * p.Nq + qrow;
+      float* prow = p.po + row * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(f32x4*)(prow + db * 32 + 8 * g + 4 * hi) =
+              (f32x4){acc_o[qb][db][4 * g] * inv, acc_o[qb][db][4 * g + 1] * inv, acc_o[qb][db][4 * g + 2] * inv,
+                      acc_o[qb][db][4 * g + 3] * inv};
+      if (hi == 0) p.plse[row] = lse;
+    } else {
+      short* orow = sl.o + (int64_t)qrow * p.o_sr;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          e16x2 lo = __builtin_convertvector((f32x2){acc_o[qb][db][4 * g + 0] * inv, acc_o[qb][db][4 * g + 1] * inv}, e16x2);
+          e16x2 up = __builtin_convertvector((f32x2){acc_o[qb][db][4 * g + 2] * inv, acc_o[qb][db][4 * g + 3] * inv}, e16x2);
+          *(u32x2*)(orow + db * 32 + 8 * g + 4 * hi) =
+              (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, up)};
+        }
+      if (hi == 0) p.lse[(int64_t)bh * p.Nq + qrow] = lse;
+    }
+  }
+}
+
 // Two waves per SIMD: one wave's MFMAs run while the other does its softmax. The
 // register budget (<= 256 per lane) is part of the kernel's design, not a hint.
 constexpr int WAVES_PER_SIMD = 2;
@@ -195,18 +271,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   __shared__ __attribute__((aligned(1024))) short lds_v0[TILE];
   __shared__ __attribute__((aligned(1024))) short lds_v1[TILE];
 
-  // Workgroups are dispatched to the 8 XCDs round-robin (blockIdx % 8). Give each
-  // XCD a contiguous range of work items so that the query blocks of one head
-  // share that XCD's L2 while they stream the same K and V.
-  const int bid = blockIdx.x;
-  const int T = p.total_wgs;
-  const int xcd = bid & 7, slot = bid >> 3, per = T >> 3, rem = T & 7;
-  const int w = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-  const int bh = w / p.num_m_blocks;
-  int mb = w - bh * p.num_m_blocks;
-  if (CAUSAL) mb = p.num_m_blocks - 1 - mb;   // longest rows first
-  const int Nq = p.Nq, Nk = p.Nk, off = p.causal_off;
-  const int m0 = mb * BM;
+  const WorkItem wi = work_item<CAUSAL>(p);
+  const int bh = wi.bh;
+  const int Nk = p.Nk, off = p.causal_off;
+  const int m0 = wi.mb * BM;
+  // keys [kb, ke) of this workgroup's range
+  const int kb = wi.split * p.split_keys;
+  const int ke = min(Nk, kb + p.split_keys);
   const Slice sl = slice_of(p, bh);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(sl.q, p.q_bytes);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(sl.k, p.k_bytes);
@@ -289,12 +360,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   for (int qb = 0; qb < QB; ++qb) { ref[qb] = -INFINITY; nb[qb] = 0.f; l_run[qb] = 0.f; }
   i16x8 pprev[QB][BN / 16];   // P of the previous tile as 16-bit B operands
 
-  // Tiles [0, n_full) need no mask for any query of this workgroup; the rest
-  // (the causal diagonal band and the ragged last tile) do. Under a causal mask the
-  // workgroup's last query sees keys up to m0 + BM - 1 + off; none may be visible.
-  const int n_end = CAUSAL ? max(0, min(Nk, m0 + BM + off)) : Nk;
-  const int ntiles = (n_end + BN - 1) / BN;
-  int n_full = (CAUSAL ? max(0, min(Nk, m0 + 1 + off)) : Nk) / BN;   // keys < n_full*BN: valid for every query
+  // Tile j holds keys kb + j BN ... Tiles [0, n_full) need no mask for any query of
+  // this workgroup; the rest (the causal diagonal band and the ragged last tile) do.
+  // Under a causal mask the workgroup's last query sees keys up to m0 + BM - 1 + off;
+  // none may be visible.
+  const int n_end = CAUSAL ? min(ke, m0 + BM + off) : ke;
+  const int ntiles = n_end > kb ? (n_end - kb + BN - 1) / BN : 0;
+  const int full_end = CAUSAL ? min(ke, m0 + 1 + off) : ke;   // keys below it: valid for every query
+  int n_full = full_end > kb ? (full_end - kb) / BN : 0;
   if (n_full > ntiles) n_full = ntiles;
 
   auto pv = [&](const short* vbuf) {
@@ -422,14 +495,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   // Tile j reads K(j) from stage j%2 and V(j-1) from stage (j-1)%2 while the direct
   // loads fill K(j+1) into stage (j+1)%2 and V(j) into stage j%2.
   auto full_tile = [&](int j, short* k_rd, short* k_wr, short* v_rd, short* v_wr, auto prev_tag) {
-    const int n0 = j * BN;
+    const int n0 = kb + j * BN;
     sync_tile();
     if (j + 1 < ntiles) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
     issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
     step(n0, k_rd, v_rd, std::false_type{}, prev_tag);
   };
   bool have_prev = false;   // pprev holds the weights of tile j-1 (wave-uniform)
-  if (ntiles > 0) issue_tile_load(rk, dma_off_k, p.k_sr, lds_k0, 0);
+  if (ntiles > 0) issue_tile_load(rk, dma_off_k, p.k_sr, lds_k0, kb);
   int j = 0;
   if (n_full > 0) {
     full_tile(0, lds_k0, lds_k1, lds_v1, lds_v0, std::false_type{});
@@ -445,7 +518,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     have_prev = true;
   }
   for (; j < ntiles; ++j) {
-    const int n0 = j * BN;
+    const int n0 = kb + j * BN;
     short* k_rd = (j & 1) ? lds_k1 : lds_k0;
     short* k_wr = (j & 1) ? lds_k0 : lds_k1;
     short* v_rd = (j & 1) ? lds_v0 : lds_v1;
@@ -466,30 +539,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   if (have_prev) pv(((ntiles - 1) & 1) ? lds_v1 : lds_v0);
 
   // ---- epilogue: O = U / l, LSE = ln2 (ref + log2 l) ----
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = wq0 + 32 * qb + l32;
-    const float l_tot = sum_halves(l_run[qb]);
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    if (qrow < Nq) {
-      short* orow = sl.o + (int64_t)qrow * p.o_sr;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          // acc_o[qb][db][4g + e] holds O^T[d = 32 db + 8 g + 4 hi + e][qrow]
-          e16x2 lo = __builtin_convertvector((f32x2){acc_o[qb][db][4 * g + 0] * inv, acc_o[qb][db][4 * g + 1] * inv}, e16x2);
-          e16x2 up = __builtin_convertvector((f32x2){acc_o[qb][db][4 * g + 2] * inv, acc_o[qb][db][4 * g + 3] * inv}, e16x2);
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          *(u32x2*)(orow + db * 32 + 8 * g + 4 * hi) =
-              (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, up)};
-        }
-      if (hi == 0) {
-        const float lse = (l_tot > 0.f) ? kLn2 * (ref[qb] + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
-        p.lse[(int64_t)bh * Nq + qrow] = lse;
-      }
-    }
-  }
+  write_rows<D, BF16, QB>(p, sl, bh, wi.split, wq0, lane, acc_o, ref, l_run);
 }
 
 // ------------------------------------------------------------------------------------
@@ -549,16 +599,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   short* const lds_v0 = lds + 2 * TILE;
   short* const lds_v1 = lds + 3 * TILE;
 
-  // ---- work item (XCD-contiguous, causal heavy-first) ----
-  const int bid = blockIdx.x;
-  const int T_all = p.total_wgs;
-  const int xcd = bid & 7, slot = bid >> 3, per = T_all >> 3, rem = T_all & 7;
-  const int w = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-  const int bh = w / p.num_m_blocks;
-  int mb = w - bh * p.num_m_blocks;
-  if (CAUSAL) mb = p.num_m_blocks - 1 - mb;
+  // ---- work item ----
+  const WorkItem wi = work_item<CAUSAL>(p);
+  const int bh = wi.bh;
   const int Nq = p.Nq, Nk = p.Nk, off = p.causal_off;
-  const int m0 = mb * BM;
+  const int m0 = wi.mb * BM;
+  const int kb = wi.split * p.split_keys;      // keys [kb, ke) of this workgroup's range
+  const int ke = min(Nk, kb + p.split_keys);
   const Slice sl = slice_of(p, bh);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(sl.q, p.q_bytes);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(sl.k, p.k_bytes);
@@ -574,14 +621,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wq0 = m0 + 32 * QB * (2 * (wave & 3) + grp);
   const float c = p.c;
 
-  // tiles the workgroup streams, tiles this wave computes, tiles it needs no mask for
-  const int n_end = CAUSAL ? max(0, min(Nk, m0 + BM + off)) : Nk;
-  const int T = (n_end + BN - 1) / BN;
+  // tiles the workgroup streams, tiles this wave computes, tiles it needs no mask
+  // for; tile j holds keys kb + j BN ...
+  const int n_end = CAUSAL ? min(ke, m0 + BM + off) : ke;
+  const int T = n_end > kb ? (n_end - kb + BN - 1) / BN : 0;
   int Tw = 0, n_full = 0;
   if (wq0 < Nq) {
-    const int w_end = CAUSAL ? max(0, min(Nk, wq0 + 32 * QB + off)) : Nk;
-    Tw = (w_end + BN - 1) / BN;
-    n_full = min(Tw, (CAUSAL ? max(0, min(Nk, wq0 + 1 + off)) : Nk) / BN);
+    const int w_end = CAUSAL ? min(ke, wq0 + 32 * QB + off) : ke;
+    Tw = w_end > kb ? (w_end - kb + BN - 1) / BN : 0;
+    const int full_end = CAUSAL ? min(ke, wq0 + 1 + off) : ke;
+    n_full = min(Tw, full_end > kb ? (full_end - kb) / BN : 0);
   }
 
   // ---- LDS fragment offsets (elements), as in fa_fwd_kernel ----
@@ -621,11 +670,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (dma_is_k[t]) {
         if (has_k)
           buffer_load16_to_lds(rk, kdst + 512 * dma_chunk[t], dma_off[t],
-                               (uint32_t)((jk * BN + ROWS_PER_DMA * dma_chunk[t]) * p.k_sr * 2));
+                               (uint32_t)((kb + jk * BN + ROWS_PER_DMA * dma_chunk[t]) * p.k_sr * 2));
       } else {
         if (has_v)
           buffer_load16_to_lds(rv, vdst + 512 * dma_chunk[t], dma_off[t],
-                               (uint32_t)((jv * BN + ROWS_PER_DMA * dma_chunk[t]) * p.v_sr * 2));
+                               (uint32_t)((kb + jv * BN + ROWS_PER_DMA * dma_chunk[t]) * p.v_sr * 2));
       }
     }
   };
@@ -797,7 +846,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     read_k(k_next);
     read_v(v_cur);
     if (j < Tw) {
-      softmax(j * BN, j >= n_full);
+      softmax(kb + j * BN, j >= n_full);
     } else {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -849,30 +898,88 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // (its P is zero unless this wave computed the last tile)
 #pragma unroll
   for (int i = 0; i < NPV; ++i) pv_step(i);
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = wq0 + 32 * qb + l32;
-    const float l_tot = sum_halves(l_run[qb]);
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    if (qrow < Nq) {
-      short* orow = sl.o + (int64_t)qrow * p.o_sr;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          e16x2 lo = __builtin_convertvector((f32x2){acc_o[qb][db][4 * g + 0] * inv, acc_o[qb][db][4 * g + 1] * inv}, e16x2);
-          e16x2 up = __builtin_convertvector((f32x2){acc_o[qb][db][4 * g + 2] * inv, acc_o[qb][db][4 * g + 3] * inv}, e16x2);
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          *(u32x2*)(orow + db * 32 + 8 * g + 4 * hi) =
-              (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, up)};
-        }
-      if (hi == 0) {
-        const float lse = (l_tot > 0.f) ? kLn2 * (ref[qb] + __builtin_amdgcn_logf(l_tot)) : -INFINITY;
-        p.lse[(int64_t)bh * Nq + qrow] = lse;
-      }
-    }
-  }
+  write_rows<D, BF16, QB>(p, sl, bh, wi.split, wq0, lane, acc_o, ref, l_run);
   if (grp == 0) phase_end(false);            // G0 matches G1's barrier count
+}
+
+// ------------------------------------------------------------------------------------
+// Split-KV merge
+// ------------------------------------------------------------------------------------
+//
+// Each key range k of a query row left O_k (normalised by its own l_k) and LSE_k.
+// Their combination is the attention over all keys: with LSE = ln sum_k e^(LSE_k),
+// O = sum_k e^(LSE_k - LSE) O_k; a range with no visible key has LSE_k = -inf and
+// weight 0, and a row with none at all gets O = 0, LSE = -inf. Memory-bound work:
+// D / 2 lanes per row, two columns each. The lanes of a row share the LSE pass (each
+// takes every (D/2)-th range, then a butterfly reduction) and leave the weights in
+// LDS; the O pass issues its loads several ranges ahead.
+constexpr int kMaxSplits = 256;
+
+struct MergeParams {
+  const float* po;
+  const float* plse;
+  short* o;
+  float* lse;
+  int rows;           // slices * Nq
+  int Nq, Hq, splits;
+  int o_sr;
+  int64_t o_sb, o_sh;
+};
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
+#pragma clang fp contract(off)
+  constexpr int LPR = D / 2;                 // lanes per row
+  constexpr int RPB = 256 / LPR;             // rows per workgroup
+  using f32x2 = float __attribute__((ext_vector_type(2)));
+  using e16x2 = typename std::conditional<BF16, __bf16 __attribute__((ext_vector_type(2))),
+                                          _Float16 __attribute__((ext_vector_type(2)))>::type;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ float wts[RPB][kMaxSplits];
+  const int rl = (int)threadIdx.x / LPR;     // row within the workgroup
+  const int j = (int)threadIdx.x % LPR;      // lane within the row
+  const int row = blockIdx.x * RPB + rl;
+  const bool live = row < m.rows;
+  const int64_t stride = m.rows;             // between the partials of consecutive ranges
+  float mx = -INFINITY;
+  if (live)
+    for (int k = j; k < m.splits; k += LPR) mx = fmaxf(mx, m.plse[k * stride + row]);
+#pragma unroll
+  for (int w = LPR / 2; w > 0; w >>= 1) mx = fmaxf(mx, __shfl_xor(mx, w, LPR));
+  float sum = 0.f;
+  if (live && mx != -INFINITY)
+    for (int k = j; k < m.splits; k += LPR) {
+      const float e = __builtin_amdgcn_exp2f((m.plse[k * stride + row] - mx) * kLog2e);
+      wts[rl][k] = e;
+      sum += e;
+    }
+#pragma unroll
+  for (int w = LPR / 2; w > 0; w >>= 1) sum += __shfl_xor(sum, w, LPR);
+  __syncthreads();
+  if (!live) return;
+  f32x2 acc = {0.f, 0.f};
+  float lse = -INFINITY;
+  if (mx != -INFINITY) {                     // sum >= 1: the maximal range contributes 1
+    const float* src = m.po + (int64_t)row * D + 2 * j;
+    const int64_t step = stride * D;
+    int k = 0;
+    for (; k + 8 <= m.splits; k += 8) {
+      f32x2 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = *(const f32x2*)(src + (k + u) * step);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += wts[rl][k + u] * x[u];
+    }
+    for (; k < m.splits; ++k) acc += wts[rl][k] * *(const f32x2*)(src + k * step);
+    const float inv = 1.f / sum;
+    acc *= inv;
+    lse = mx + kLn2 * __builtin_amdgcn_logf(sum);
+  }
+  const int bh = row / m.Nq, i = row - bh * m.Nq;
+  const int b = bh / m.Hq, h = bh - b * m.Hq;
+  short* orow = m.o + b * m.o_sb + h * m.o_sh + (int64_t)i * m.o_sr + 2 * j;
+  *(uint32_t*)orow = __builtin_bit_cast(uint32_t, __builtin_convertvector(acc, e16x2));
+  if (j == 0) m.lse[row] = lse;
 }
 
 // ------------------------------------------------------------------------------------
@@ -887,6 +994,13 @@ constexpr TileShape kTiles[] = {
     {64, 64, 2, 1, true}, {128, 64, 4, 1, true}, {128, 32, 4, 1, true},
     // fa_fwd_pp_kernel: 8 waves in two groups taking turns on each SIMD's matrix pipe
     {256, 32, 8, 1, true}, {256, 64, 8, 1, false}, {512, 32, 8, 2, false}};
+
+template <int D, bool BF16>
+hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
+  constexpr int RPB = 256 / (D / 2);
+  hipLaunchKernelGGL((fa_merge_kernel<D, BF16>), dim3((m.rows + RPB - 1) / RPB), dim3(256), 0, stream, m);
+  return hipGetLastError();
+}
 
 template <int D, bool BF16, bool CAUSAL, int NW, int QB, int BN>
 hipError_t launch_one(const Params& p, hipStream_t stream) {
@@ -948,62 +1062,6 @@ fa_status read_strides(const int64_t* st, int64_t H, int64_t N, int64_t d, int64
   return FA_OK;
 }
 
-fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
-              int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, const int64_t* qs_in, const int64_t* ks_in,
-              const int64_t* vs_in, const int64_t* os_in, float scale, int causal, fa_dtype dtype,
-              void* stream, int bm, int bn) {
-  if (B < 0 || Hq < 0 || Hk < 0 || Nq < 0 || Nk < 0) return FA_ERR_BAD_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
-  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_BAD_SCALE;
-  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_BAD_DTYPE;
-  if (!tile_ok(d, bm, bn)) return FA_ERR_UNSUPPORTED_TILE;
-  if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
-  if (Hk == 0 || Hq % Hk != 0) return FA_ERR_BAD_SHAPE;
-  if (!q || !o || !lse) return FA_ERR_NULL_PTR;
-  if (Nk > 0 && (!k || !v)) return FA_ERR_NULL_PTR;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_MISALIGNED;
-  if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
-  int64_t qs[3], ks[3], vs[3], os[3];
-  fa_status st;
-  if ((st = read_strides(qs_in, Hq, Nq, d, qs)) != FA_OK) return st;
-  if ((st = read_strides(ks_in, Hk, Nk, d, ks)) != FA_OK) return st;
-  if ((st = read_strides(vs_in, Hk, Nk, d, vs)) != FA_OK) return st;
-  if ((st = read_strides(os_in, Hq, Nq, d, os)) != FA_OK) return st;
-  if (!rows_fit(Nq, qs[2]) || !rows_fit(Nq, os[2]) || !rows_fit(Nk, ks[2]) || !rows_fit(Nk, vs[2]))
-    return FA_ERR_TOO_LARGE;
-  const int64_t mblocks = (Nq + bm - 1) / bm;
-  if (B >= ((int64_t)1 << 31) || Hq >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
-  if (B * Hq >= ((int64_t)1 << 31) / mblocks + 1) return FA_ERR_TOO_LARGE;
-  const int64_t total = B * Hq * mblocks;
-  if (total >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
-  Params p;
-  p.q = (const short*)q;
-  p.k = (const short*)k;
-  p.v = (const short*)v;
-  p.o = (short*)o;
-  p.lse = lse;
-  p.Nq = (int)Nq;
-  p.Nk = (int)Nk;
-  p.Hq = (int)Hq;
-  p.group = (int)(Hq / Hk);
-  p.causal_off = (int)(Nk - Nq);   // bottom-right alignment; 0 (top-left) when Nq = Nk
-  p.q_sb = qs[0]; p.q_sh = qs[1]; p.q_sr = (int)qs[2];
-  p.k_sb = ks[0]; p.k_sh = ks[1]; p.k_sr = (int)ks[2];
-  p.v_sb = vs[0]; p.v_sh = vs[1]; p.v_sr = (int)vs[2];
-  p.o_sb = os[0]; p.o_sh = os[1]; p.o_sr = (int)os[2];
-  p.q_bytes = (uint32_t)((Nq - 1) * qs[2] + d) * 2;
-  p.k_bytes = Nk > 0 ? (uint32_t)((Nk - 1) * ks[2] + d) * 2 : 0;
-  p.v_bytes = Nk > 0 ? (uint32_t)((Nk - 1) * vs[2] + d) * 2 : 0;
-  p.num_m_blocks = (int)mblocks;
-  p.total_wgs = (int)total;
-  p.c = (float)((double)scale * 1.4426950408889634);  // s * log2(e), rounded once
-  const hipStream_t s = (hipStream_t)stream;
-  const bool bf16 = dtype == FA_BF16;
-  hipError_t e = (d == 64) ? launch_d<64>(p, bf16, causal != 0, bm, bn, s)
-                           : launch_d<128>(p, bf16, causal != 0, bm, bn, s);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
-}
-
 void default_tile(int64_t N, int64_t d, int causal, int* bm, int* bn) {
   // Measured on MI355X (interleaved tile sweeps per workload family):
   //  - short sequences: the smallest tile, so that more workgroups exist;
@@ -1024,6 +1082,148 @@ void default_tile(int64_t N, int64_t d, int causal, int* bm, int* bn) {
   }
 }
 
+
+// Resident workgroups per CU: the four-wave tiles run two waves per SIMD (2 per CU),
+// the eight-wave tiles one workgroup per CU; the 2-wave (64, 64) tile fits two waves
+// per SIMD at d = 64 (4 per CU) but needs more than 256 registers at d = 128 (2 per CU).
+int wgs_per_cu(int bm, int64_t d) {
+  if (bm == 64) return d == 64 ? 4 : 2;
+  return bm == 128 ? 2 : 1;
+}
+
+// Key ranges per query block for split-KV. Measured on MI355X: a split pays when the
+// query blocks leave resident workgroup slots empty, and pays best when every slot is
+// filled once (a second round of workgroups costs more than the shorter ranges save)
+// with ranges of at least 8 key tiles, below which the per-workgroup prologue and
+// the merge dominate. Decoding-like shapes (a single, mostly empty query block per
+// slice) stream K and V at the memory's pace and do best with one workgroup per CU.
+int split_heuristic(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d, int bm, int bn) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0 || Nk <= 0) return 1;
+  const int64_t base = B * Hq * ((Nq + bm - 1) / bm);
+  const int64_t slots = 256 * (int64_t)(2 * Nq <= bm ? 1 : wgs_per_cu(bm, d));
+  if (base >= slots) return 1;
+  const int64_t tiles = (Nk + bn - 1) / bn;
+  int64_t sp = slots / base;
+  if (sp > tiles / 8) sp = tiles / 8;
+  if (sp > kMaxSplits) sp = kMaxSplits;
+  return sp < 1 ? 1 : (int)sp;
+}
+
+// Everything fa_fwd, fa_fwd_ex and fa_fwd_split share. num_splits = 1: one workgroup
+// per query block, written straight to o and lse; otherwise partials in workspace
+// and a merge launch.
+fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
+              int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, const int64_t* qs_in, const int64_t* ks_in,
+              const int64_t* vs_in, const int64_t* os_in, float scale, int causal, fa_dtype dtype,
+              void* stream, int bm, int bn, int num_splits = 1, void* workspace = nullptr,
+              size_t workspace_bytes = 0) {
+  if (B < 0 || Hq < 0 || Hk < 0 || Nq < 0 || Nk < 0) return FA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_BAD_DTYPE;
+  const bool auto_tile = bm == 0 && bn == 0;
+  if (!auto_tile && !tile_ok(d, bm, bn)) return FA_ERR_UNSUPPORTED_TILE;
+  if (num_splits < 1 || num_splits > kMaxSplits) return FA_ERR_BAD_SPLITS;
+  if (B == 0 || Hq == 0 || Nq == 0) return FA_OK;
+  if (Hk == 0 || Hq % Hk != 0) return FA_ERR_BAD_SHAPE;
+  if (!q || !o || !lse) return FA_ERR_NULL_PTR;
+  if (Nk > 0 && (!k || !v)) return FA_ERR_NULL_PTR;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  fa_status st;
+  if ((st = read_strides(qs_in, Hq, Nq, d, qs)) != FA_OK) return st;
+  if ((st = read_strides(ks_in, Hk, Nk, d, ks)) != FA_OK) return st;
+  if ((st = read_strides(vs_in, Hk, Nk, d, vs)) != FA_OK) return st;
+  if ((st = read_strides(os_in, Hq, Nq, d, os)) != FA_OK) return st;
+  int64_t group = Hq / Hk;
+  // Decoding with grouped K/V heads: a single query row per head, so the query heads
+  // that share a K/V head become the rows of one slice (their rows are one head
+  // stride apart, and the lse rows [B, Hq, 1] are [B, Hk, group]). With one query
+  // row the bottom-right causal mask hides no key.
+  if (Nq == 1 && group > 1) {
+    qs[2] = qs[1];          // row r of the packed slice: query head r of the group
+    os[2] = os[1];
+    qs[1] *= group;         // next slice: the next group of query heads
+    os[1] *= group;
+    Nq = group;
+    Hq = Hk;
+    group = 1;
+    causal = 0;
+  }
+  if (auto_tile) default_tile(Nq, d, causal, &bm, &bn);
+  if (!rows_fit(Nq, qs[2]) || !rows_fit(Nq, os[2]) || !rows_fit(Nk, ks[2]) || !rows_fit(Nk, vs[2]))
+    return FA_ERR_TOO_LARGE;
+  if (B >= ((int64_t)1 << 31) || Hq >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
+  const int64_t slices = B * Hq;
+  if (slices >= ((int64_t)1 << 31) / Nq + 1) return FA_ERR_TOO_LARGE;   // rows = slices * Nq < 2^31
+  const int64_t mblocks = (Nq + bm - 1) / bm;
+  // key ranges: a whole number of tiles each, none empty
+  const int64_t tiles = (Nk + bn - 1) / bn;
+  int64_t splits = num_splits < tiles ? num_splits : (tiles > 0 ? tiles : 1);
+  int64_t split_keys = ((tiles + splits - 1) / splits) * bn;
+  if (Nk > 0) splits = (Nk + split_keys - 1) / split_keys;
+  if (splits == 1) split_keys = tiles * bn;
+  const int64_t total = slices * mblocks * splits;
+  if (total >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
+  float* po = nullptr;
+  float* plse = nullptr;
+  if (splits > 1) {
+    const int64_t rows = slices * Nq;
+    const uint64_t need = (uint64_t)splits * rows * (d + 1) * 4;
+    if (!workspace || ((uintptr_t)workspace & 15) || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    po = (float*)workspace;
+    plse = po + splits * rows * d;
+  }
+  Params p;
+  p.q = (const short*)q;
+  p.k = (const short*)k;
+  p.v = (const short*)v;
+  p.o = (short*)o;
+  p.lse = lse;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.Hq = (int)Hq;
+  p.group = (int)group;
+  p.causal_off = (int)(Nk - Nq);   // bottom-right alignment; 0 (top-left) when Nq = Nk
+  p.q_sb = qs[0]; p.q_sh = qs[1]; p.q_sr = (int)qs[2];
+  p.k_sb = ks[0]; p.k_sh = ks[1]; p.k_sr = (int)ks[2];
+  p.v_sb = vs[0]; p.v_sh = vs[1]; p.v_sr = (int)vs[2];
+  p.o_sb = os[0]; p.o_sh = os[1]; p.o_sr = (int)os[2];
+  p.q_bytes = (uint32_t)((Nq - 1) * qs[2] + d) * 2;
+  p.k_bytes = Nk > 0 ? (uint32_t)((Nk - 1) * ks[2] + d) * 2 : 0;
+  p.v_bytes = Nk > 0 ? (uint32_t)((Nk - 1) * vs[2] + d) * 2 : 0;
+  p.num_m_blocks = (int)mblocks;
+  p.num_splits = (int)splits;
+  p.split_keys = (int)split_keys;
+  p.slices = (int)slices;
+  p.total_wgs = (int)total;
+  p.c = (float)((double)scale * 1.4426950408889634);  // s * log2(e), rounded once
+  p.po = po;
+  p.plse = plse;
+  const hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dtype == FA_BF16;
+  hipError_t e = (d == 64) ? launch_d<64>(p, bf16, causal != 0, bm, bn, s)
+                           : launch_d<128>(p, bf16, causal != 0, bm, bn, s);
+  if (e == hipSuccess && splits > 1) {
+    MergeParams m;
+    m.po = po;
+    m.plse = plse;
+    m.o = (short*)o;
+    m.lse = lse;
+    m.rows = (int)(slices * Nq);
+    m.Nq = (int)Nq;
+    m.Hq = (int)Hq;
+    m.splits = (int)splits;
+    m.o_sr = (int)os[2];
+    m.o_sb = os[0];
+    m.o_sh = os[1];
+    if (d == 64) e = bf16 ? launch_merge<64, true>(m, s) : launch_merge<64, false>(m, s);
+    else e = bf16 ? launch_merge<128, true>(m, s) : launch_merge<128, false>(m, s);
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1040,6 +1240,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 fa_status fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                        int64_t H, int64_t N, int64_t d, float scale, int causal, fa_dtype dtype,
                        void* stream, int block_m, int block_n) {
+  if (block_m == 0 && block_n == 0) block_m = -1;   // no automatic choice here: (0, 0) is not a tile
   return run(q, k, v, o, lse, B, H, H, N, N, d, nullptr, nullptr, nullptr, nullptr, scale, causal, dtype,
              stream, block_m, block_n);
 }
@@ -1048,9 +1249,36 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
                     int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, const int64_t* q_strides,
                     const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
                     float scale, int causal, fa_dtype dtype, void* stream, int block_m, int block_n) {
-  if (block_m == 0 && block_n == 0) default_tile(Nq, d, causal, &block_m, &block_n);
   return run(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, q_strides, k_strides, v_strides, o_strides, scale,
              causal, dtype, stream, block_m, block_n);
+}
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                       int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, const int64_t* q_strides,
+                       const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
+                       float scale, int causal, fa_dtype dtype, void* stream, int block_m, int block_n,
+                       int num_splits, void* workspace, size_t workspace_bytes) {
+  return run(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, q_strides, k_strides, v_strides, o_strides, scale,
+             causal, dtype, stream, block_m, block_n, num_splits, workspace, workspace_bytes);
+}
+
+size_t fa_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d, int num_splits) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0 || (d != 64 && d != 128) || num_splits < 1 || num_splits > kMaxSplits) return 0;
+  if (num_splits == 1) return 0;
+  return (size_t)num_splits * (size_t)(B * Hq * Nq) * (size_t)(d + 1) * 4;
+}
+
+int fa_split_default(int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                     int block_m, int block_n) {
+  if (B <= 0 || Hq <= 0 || Hk <= 0 || Hq % Hk || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 1;
+  if (Nq == 1 && Hq > Hk) {   // decoding with grouped heads: the group forms one slice
+    Nq = Hq / Hk;
+    Hq = Hk;
+    causal = 0;
+  }
+  if (block_m == 0 && block_n == 0) default_tile(Nq, d, causal, &block_m, &block_n);
+  if (!tile_ok(d, block_m, block_n)) return 1;
+  return split_heuristic(B, Hq, Nq, Nk, d, block_m, block_n);
 }
 
 int fa_tile_supported(int64_t d, int block_m, int block_n) { return tile_ok(d, block_m, block_n) ? 1 : 0; }
@@ -1077,6 +1305,8 @@ const char* fa_status_str(int status) {
     case FA_ERR_UNSUPPORTED_TILE: return "tile shape not compiled";
     case FA_ERR_HIP: return "HIP launch error";
     case FA_ERR_BAD_STRIDE: return "strides must be non-negative multiples of 8 elements, row stride >= d";
+    case FA_ERR_BAD_SPLITS: return "num_splits must be between 1 and 256";
+    case FA_ERR_WORKSPACE: return "split-KV workspace missing, not 16-byte aligned or smaller than fa_split_workspace_bytes";
     default: return "unknown status";
   }
 }

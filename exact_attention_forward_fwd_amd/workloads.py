@@ -69,6 +69,74 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class GeneralWorkload:
+    """A workload of the general and split-KV entry points: Hq query heads over Hk K/V
+    heads, Nq queries against Nk keys (causal = bottom-right alignment)."""
+    index: int                 # seed = 1000 + index
+    name: str
+    B: int
+    Hq: int
+    Hk: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: bool
+    scale: float
+    v_std: float = 1.0
+
+    @property
+    def torch_dtype(self):
+        return torch.float16 if self.dtype == "f16" else torch.bfloat16
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+    @property
+    def visible_pairs(self) -> int:
+        """(query, key) pairs the mask leaves visible, per (batch, head)."""
+        if not self.causal:
+            return self.Nq * self.Nk
+        off = self.Nk - self.Nq
+        return sum(max(0, min(self.Nk, i + off + 1)) for i in range(self.Nq))
+
+    @property
+    def flops(self) -> float:
+        """4 d FLOPs per visible (query, key) pair and head (both products)."""
+        return 4.0 * self.d * self.B * self.Hq * self.visible_pairs
+
+    @property
+    def hbm_bytes(self) -> int:
+        """Compulsory traffic: Q, K, V read once, O and LSE written once."""
+        e = 2
+        return (2 * self.B * self.Hq * self.Nq * self.d * e + 2 * self.B * self.Hk * self.Nk * self.d * e
+                + 4 * self.B * self.Hq * self.Nq)
+
+
+# Split-KV workloads: long-context decoding (one new query row per head against a
+# 128K-key cache, grouped K/V heads: ch. 14 §14.7.1's case), and one GPU's share of
+# the N = 16384 workload when its 16 heads are divided over 8 GPUs (2 heads each).
+SPLIT_WORKLOADS = {
+    6: GeneralWorkload(6, "decode_nk131072_hq32_hk8_d128_bf16", 1, 32, 8, 1, 131072, 128, "bf16", True,
+                       1 / math.sqrt(128)),
+    7: GeneralWorkload(7, "n16384_d128_bf16_h2_shard", 1, 2, 2, 16384, 16384, 128, "bf16", False,
+                       1 / math.sqrt(128)),
+}
+
+
+def make_general_inputs(w: GeneralWorkload):
+    """(q, k, v) CPU tensors: q [B, Hq, Nq, d], k and v [B, Hk, Nk, d]; Q, K ~ N(0, 1),
+    V ~ N(0, v_std^2), drawn in that order in float32 and rounded to the 16-bit type."""
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    q = torch.randn((w.B, w.Hq, w.Nq, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.Hk, w.Nk, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.Hk, w.Nk, w.d), generator=g, dtype=torch.float32) * w.v_std
+    dt = w.torch_dtype
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
 def spike_count(w: Workload) -> int:
     return int(round(w.spike_frac * w.N))
 

@@ -23,6 +23,7 @@
 #define FA_MI355X_FA_H
 
 #include <stdint.h>
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -42,10 +43,12 @@ typedef enum {
   FA_ERR_BAD_SCALE = 4,          /* scale is not finite or not > 0 */
   FA_ERR_BAD_DTYPE = 5,          /* dtype is not FA_F16 / FA_BF16 */
   FA_ERR_MISALIGNED = 6,         /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
-  FA_ERR_TOO_LARGE = 7,          /* (N + 512) * row stride >= 2^30 elements, or the grid exceeds 2^31-1 workgroups */
+  FA_ERR_TOO_LARGE = 7,          /* (N + 512) * row stride >= 2^30 elements, B * H * N >= 2^31, or the grid exceeds 2^31-1 workgroups */
   FA_ERR_UNSUPPORTED_TILE = 8,   /* (block_m, block_n) not among the compiled tile shapes */
   FA_ERR_HIP = 9,                /* the HIP runtime reported an error at launch */
-  FA_ERR_BAD_STRIDE = 10         /* a stride is negative or not a multiple of 8 elements, or a row stride < d */
+  FA_ERR_BAD_STRIDE = 10,        /* a stride is negative or not a multiple of 8 elements, or a row stride < d */
+  FA_ERR_BAD_SPLITS = 11,        /* num_splits outside [1, 256] */
+  FA_ERR_WORKSPACE = 12          /* split-KV workspace NULL, not 16-byte aligned or too small */
 } fa_status;
 
 /*
@@ -123,6 +126,49 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
                     const int64_t* v_strides, const int64_t* o_strides,
                     float scale, int causal, fa_dtype dtype, void* stream,
                     int block_m, int block_n);
+
+/*
+ * fa_fwd_split — fa_fwd_ex with the keys of every query block divided into up to
+ * num_splits ranges, each handled by its own workgroup (split-KV: "CUDA 算子工程：手写
+ * FlashAttention v2 之路" ch. 14, §14.7.1, for long key sequences with few query
+ * blocks, as in decoding, where one workgroup per query block would leave most of the
+ * GPU idle). Range k of a row leaves its partial output O_k = U_k / l_k (fp32) and
+ * LSE_k in `workspace`; a second kernel on the same stream merges them with the
+ * online-softmax algebra of "用 CuTe 读懂 FlashAttention" step 4 applied to whole
+ * ranges: LSE = ln sum_k exp(LSE_k), O = sum_k exp(LSE_k - LSE) O_k.
+ *
+ *   num_splits: 1..256. The ranges are whole key tiles, so fewer ranges than asked
+ *             are used when Nk has fewer tiles; 1 is exactly fa_fwd_ex (no workspace
+ *             needed). fa_split_default suggests a count.
+ *   workspace: device memory owned by the caller, 16-byte aligned, of at least
+ *             fa_split_workspace_bytes(B, Hq, Nq, d, num_splits) bytes. Its contents
+ *             on entry do not matter; it is in use until the merge kernel has run (stream
+ *             order), so calls that overlap on different streams need separate
+ *             workspaces. May be NULL when no split is made.
+ *   Other arguments, results and errors as fa_fwd_ex; additionally FA_ERR_BAD_SPLITS
+ *   and FA_ERR_WORKSPACE. The result equals fa_fwd_ex's up to rounding.
+ *
+ * With Nq = 1 and Hq > Hk (decoding with grouped K/V heads) fa_fwd_ex and fa_fwd_split
+ * process the query heads that share a K/V head as the rows of one block, reading
+ * each K/V head once; this needs nothing of the caller.
+ */
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d,
+                       const int64_t* q_strides, const int64_t* k_strides,
+                       const int64_t* v_strides, const int64_t* o_strides,
+                       float scale, int causal, fa_dtype dtype, void* stream,
+                       int block_m, int block_n, int num_splits, void* workspace,
+                       size_t workspace_bytes);
+
+/* Workspace bytes fa_fwd_split needs for these sizes and num_splits: 4 (d + 1) bytes
+ * per range and query row; 0 if num_splits = 1 or an argument is out of range. */
+size_t fa_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d, int num_splits);
+
+/* A split count for fa_fwd_split (>= 1): the one that minimises the modelled time,
+ * rounds of resident workgroups times key tiles per workgroup. block_m, block_n as in
+ * fa_fwd_ex (0, 0: the default tile). 1 when the query blocks alone fill the GPU. */
+int fa_split_default(int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                     int block_m, int block_n);
 
 /* 1 if (block_m, block_n) is compiled for head dimension d, else 0. */
 int fa_tile_supported(int64_t d, int block_m, int block_n);

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(11):
+    for code in range(13):
         s = fa.status_str(code)
         assert s and s != "unknown status"
     assert fa.status_str(99) == "unknown status"
@@ -89,6 +89,40 @@ def test_general_entry_validation_without_gpu():
     assert call_ex(bm=96, bn=64) == 8
     assert call_ex(q=None, k=None, v=None, o=None, lse=None, Nq=0) == 0
     assert call_ex(q=None, k=None, v=None, o=None, lse=None, Hq=0, Hk=0) == 0
+
+
+def call_split(ws=None, ws_bytes=0, splits=2, q=A, B=1, Hq=4, Hk=2, Nq=64, Nk=100, d=64, causal=0, bm=0, bn=0):
+    return fa.fa_fwd_split(q, A, A, A, A, B, Hq, Hk, Nq, Nk, d, None, None, None, None, 0.125, causal, 0, None,
+                           bm, bn, splits, ws, ws_bytes)
+
+
+def test_split_entry_validation_without_gpu():
+    assert call_split(splits=0) == 11 and call_split(splits=257) == 11 and call_split(splits=-3) == 11
+    assert call_split(splits=0, Nq=0) == 11            # the split count is checked before the empty case
+    assert call_split(ws=None, ws_bytes=0) == 12       # Nk = 100 has two 64-key tiles: a split is made
+    need = fa.fa_split_workspace_bytes(1, 4, 64, 64, 2)
+    assert need == 2 * (1 * 4 * 64) * (64 + 1) * 4
+    assert call_split(ws=A, ws_bytes=need - 4) == 12   # too small
+    assert call_split(ws=A + 8, ws_bytes=need) == 12   # not 16-byte aligned
+    assert call_split(q=None, ws=A, ws_bytes=need) == 1
+    assert call_split(Hk=3, ws=A, ws_bytes=need) == 2
+    assert call_split(bm=96, bn=64, ws=A, ws_bytes=need) == 8
+    assert call_split(q=None, Nq=0) == 0               # empty: nothing to do, nothing checked further
+
+
+def test_split_sizes_and_default():
+    assert fa.fa_split_workspace_bytes(2, 8, 100, 128, 1) == 0
+    assert fa.fa_split_workspace_bytes(2, 8, 100, 96, 4) == 0
+    assert fa.fa_split_workspace_bytes(2, 8, 100, 128, 257) == 0
+    assert fa.fa_split_workspace_bytes(2, 8, 100, 128, 3) == 3 * 1600 * 129 * 4
+    # query blocks alone fill the GPU: no split
+    assert fa.fa_split_default(2, 16, 16, 4096, 4096, 64, False) == 1
+    # decoding, one query row per head, 128K keys: many ranges, within the limit
+    s = fa.fa_split_default(1, 32, 8, 1, 131072, 128, True)
+    assert 16 <= s <= 256
+    # no more ranges than key tiles
+    assert fa.fa_split_default(1, 1, 1, 64, 128, 64, False, 64, 64) <= 2
+    assert fa.fa_split_default(1, 1, 1, 64, 0, 64, False) == 1
 
 
 def test_empty_problems_need_no_pointers():
