@@ -1,4 +1,4 @@
-"""CPU oracle for exact attention forward — TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for exact attention (forward and gradients) — TEST INFRASTRUCTURE ONLY.
 
 Only the test suite, the package smoke check and the benchmark's CPU-baseline leg
 may import anything here. The product path (the HIP library and its Python
@@ -9,6 +9,8 @@ Two independent CPU codes live here:
 
 * ``attention_fwd`` / ``attention_rows`` — the definition written out in plain C,
   fp64, three passes over each stored score row (``attn_oracle.c``).
+* ``attention_bwd`` — the gradients of that definition (chain rule through the
+  softmax), in plain C fp64, independent of the forward code.
 * ``tiled.online_softmax_attention`` — the tiled online-softmax recurrence in
   numpy fp64, in the order of the FA2 forward pseudocode, used to pin the blog's
   per-round intermediate figures and as a brute-force cross-check of the C code.
@@ -53,6 +55,9 @@ def load_library(path: str):
     lib.oracle_attn_rows_f64.argtypes = [dp, dp, dp, i64, i64, i64, i64, ctypes.c_double,
                                          ctypes.c_int, ctypes.POINTER(i64), i64, dp, dp]
     lib.oracle_attn_rows_f64.restype = ctypes.c_int
+    lib.oracle_attn_bwd_f64.argtypes = [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, ctypes.c_double,
+                                        ctypes.c_int]
+    lib.oracle_attn_bwd_f64.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -141,6 +146,25 @@ def attention_rows(q, k, v, scale: float, causal: bool, rows, lib=None, align: s
     if rc != 0:
         raise ValueError(f"oracle_attn_rows_f64 failed with code {rc}")
     return o, lse
+
+
+def attention_bwd(q, k, v, dout, scale: float, causal: bool = False, lib=None, align: str = "top-left"):
+    """Exact gradients (dq, dk, dv) in fp64 of a loss L with dL/dO = ``dout`` for the
+    forward of ``attention_fwd`` (same shapes, masking and alignment): the forward
+    definition differentiated, with P recomputed from the scores (``attn_oracle.c``).
+    """
+    q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
+    lead, bh, nq, nk, d = _shape3(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must be shaped like q")
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rc = (lib or _load()).oracle_attn_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                              bh, nq, nk, d, float(scale), _causal_mode(causal, align))
+    if rc != 0:
+        raise ValueError(f"oracle_attn_bwd_f64 failed with code {rc}")
+    return dq, dk, dv
 
 
 def num_threads() -> int:

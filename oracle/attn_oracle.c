@@ -1,5 +1,6 @@
 /*
- * Plain fp64 CPU oracle for exact softmax attention (forward).
+ * Plain fp64 CPU oracle for exact softmax attention: the forward, and its gradients
+ * (oracle_attn_bwd_f64 near the end of the file).
  *
  * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or load
  * this file or the library built from it; only the test suite, the smoke check
@@ -155,6 +156,105 @@ int oracle_attn_rows_f64(const double* q, const double* k, const double* v, int6
       }
       free(z);
     }
+  }
+  return fail ? 4 : 0;
+}
+
+/*
+ * Backward pass: the gradients of a scalar loss L with respect to Q, K and V, given
+ * dO = dL/dO, for the forward defined at the top of this file.
+ *
+ * The pages define only the forward; "CUDA 算子工程" ch. 14 §14.5 says its LSE
+ * output exists for the backward pass and §14.7 gives the backward's loop order.
+ * The gradients are the forward definition differentiated (chain rule), per row i
+ * over its valid keys j, with z_ij = s q_i . k_j, P_i. = softmax(z_i.), O_i = sum_j P_ij v_j:
+ *   dL/dP_ij = dO_i . v_j                                  (dP)
+ *   dL/dz_ij = P_ij (dP_ij - sum_k P_ik dP_ik)             (softmax Jacobian; the sum is
+ *                                                           dO_i . O_i, called D_i)
+ *   dL/dq_i  = s sum_j dL/dz_ij k_j
+ *   dL/dk_j  = s sum_i dL/dz_ij q_i
+ *   dL/dv_j  = sum_i P_ij dO_i
+ * A row with no valid key has O_i = 0 whatever the inputs and contributes nothing.
+ * P is recomputed here from the scores with the row's own maximum and sum (three
+ * passes, as in the forward), not from a stored LSE.
+ *
+ * q, dout: [BH, Nq, d]; k, v: [BH, Nk, d]; dq: [BH, Nq, d]; dk, dv: [BH, Nk, d];
+ * row-major contiguous doubles owned by the caller, all outputs overwritten.
+ * Slices run in parallel; within a slice the rows run in order. Return codes as
+ * oracle_attn_fwd_f64.
+ */
+int oracle_attn_bwd_f64(const double* q, const double* k, const double* v, const double* dout,
+                        double* dq, double* dk, double* dv, int64_t BH, int64_t Nq, int64_t Nk,
+                        int64_t d, double scale, int causal) {
+  if (BH < 0 || Nq < 0 || Nk < 0 || d < 0) return 2;
+  if (!(scale > 0.0) || !isfinite(scale)) return 3;
+  if (causal < 0 || causal > 2) return 6;
+  if (BH == 0) return 0;
+  if ((Nq > 0 && (!q || !dout || !dq)) || (Nk > 0 && (!k || !v || !dk || !dv))) return 1;
+  int fail = 0;
+#pragma omp parallel
+  {
+    const size_t n = (size_t)(Nk > 0 ? Nk : 1);
+    double* z = (double*)malloc(sizeof(double) * n);
+    double* pr = (double*)malloc(sizeof(double) * n);
+    double* dp = (double*)malloc(sizeof(double) * n);
+    if (!z || !pr || !dp) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t bh = 0; bh < BH; ++bh) {
+        const double* qs = q + bh * Nq * d;
+        const double* ks = k + bh * Nk * d;
+        const double* vs = v + bh * Nk * d;
+        const double* dos = dout + bh * Nq * d;
+        double* dqs = dq + bh * Nq * d;
+        double* dks = dk + bh * Nk * d;
+        double* dvs = dv + bh * Nk * d;
+        for (int64_t t = 0; t < Nk * d; ++t) { dks[t] = 0.0; dvs[t] = 0.0; }
+        for (int64_t i = 0; i < Nq; ++i) {
+          const double* qi = qs + i * d;
+          const double* doi = dos + i * d;
+          double* dqi = dqs + i * d;
+          for (int64_t c = 0; c < d; ++c) dqi[c] = 0.0;
+          int64_t nv = Nk;
+          if (causal == 1) nv = (i + 1 < Nk) ? (i + 1) : Nk;
+          if (causal == 2) nv = (i + Nk - Nq + 1 < Nk) ? (i + Nk - Nq + 1) : Nk;
+          if (nv <= 0) continue;
+          /* scores and the row's softmax (max, sum, normalised weights) */
+          for (int64_t j = 0; j < nv; ++j) {
+            double x = 0.0;
+            for (int64_t c = 0; c < d; ++c) x += qi[c] * ks[j * d + c];
+            z[j] = scale * x;
+          }
+          double m = z[0];
+          for (int64_t j = 1; j < nv; ++j)
+            if (z[j] > m) m = z[j];
+          double l = 0.0;
+          for (int64_t j = 0; j < nv; ++j) l += exp(z[j] - m);
+          for (int64_t j = 0; j < nv; ++j) pr[j] = exp(z[j] - m) / l;
+          /* dP_ij = dO_i . v_j and D_i = sum_j P_ij dP_ij */
+          double Di = 0.0;
+          for (int64_t j = 0; j < nv; ++j) {
+            double x = 0.0;
+            for (int64_t c = 0; c < d; ++c) x += doi[c] * vs[j * d + c];
+            dp[j] = x;
+            Di += pr[j] * x;
+          }
+          for (int64_t j = 0; j < nv; ++j) {
+            const double dz = pr[j] * (dp[j] - Di);
+            for (int64_t c = 0; c < d; ++c) {
+              dqi[c] += scale * dz * ks[j * d + c];
+              dks[j * d + c] += scale * dz * qi[c];
+              dvs[j * d + c] += pr[j] * doi[c];
+            }
+          }
+        }
+      }
+    }
+    free(z);
+    free(pr);
+    free(dp);
   }
   return fail ? 4 : 0;
 }
