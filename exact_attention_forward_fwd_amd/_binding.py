@@ -22,7 +22,7 @@ STATUS_NAMES = {
     12: "FA_ERR_WORKSPACE",
 }
 EXPORTED = ("fa_fwd", "fa_fwd_tiled", "fa_fwd_ex", "fa_fwd_split", "fa_split_workspace_bytes", "fa_split_default",
-            "fa_tile_supported", "fa_default_tile", "fa_status_str")
+            "fa_bwd", "fa_bwd_workspace_bytes", "fa_tile_supported", "fa_default_tile", "fa_status_str")
 
 
 class FaError(RuntimeError):
@@ -60,6 +60,11 @@ def load_library(path: str = LIB_PATH):
     lib.fa_split_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_split_default.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, i32]
     lib.fa_split_default.restype = i32
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp,
+                           ctypes.c_size_t, vp]
+    lib.fa_bwd.restype = i32
+    lib.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_tile_supported.argtypes = [i64, i32, i32]
     lib.fa_tile_supported.restype = i32
     lib.fa_default_tile.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
@@ -116,6 +121,17 @@ def fa_split_workspace_bytes(B: int, Hq: int, Nq: int, d: int, num_splits: int) 
 def fa_split_default(B: int, Hq: int, Hk: int, Nq: int, Nk: int, d: int, causal: bool, block_m: int = 0,
                      block_n: int = 0) -> int:
     return int(load_library().fa_split_default(B, Hq, Hk, Nq, Nk, d, int(causal), int(block_m), int(block_n)))
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, workspace, workspace_bytes,
+           stream) -> int:
+    """Raw C call of the backward entry point; pointers are device addresses."""
+    return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, int(causal), dtype,
+                                 workspace, int(workspace_bytes), stream)
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, H, N))
 
 
 def fa_tile_supported(d: int, block_m: int, block_n: int) -> bool:
@@ -256,3 +272,38 @@ def fwd_split(q, k, v, scale: float | None = None, causal: bool = False, num_spl
     if st != 0:
         raise FaError(st, "fa_fwd_split")
     return out, lse
+
+
+def bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = False, dq=None, dk=None, dv=None,
+        workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of the attention forward on torch tensors [B, H, N, d]
+    (contiguous, same device and 16-bit dtype): o and lse as returned by ``fwd`` for
+    the same q, k, v, scale and causal; dout = dL/dO. ``workspace``: a device tensor of
+    at least fa_bwd_workspace_bytes(B, H, N) bytes, allocated here if None.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor [B, H, N, d]")
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must match q's shape and dtype")
+    B, H, N, d = q.shape
+    if not lse.is_contiguous() or tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fa_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), causal, _dtype_code(q),
+                workspace.data_ptr(), workspace.numel() * workspace.element_size(), sp)
+    if st != 0:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

@@ -13,7 +13,7 @@ import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
-SOURCES = [os.path.join(PKG_DIR, "csrc", "fa_fwd.hip")]
+SOURCES = [os.path.join(PKG_DIR, "csrc", "fa_fwd.hip"), os.path.join(PKG_DIR, "csrc", "fa_bwd.hip")]
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 ARCH = "gfx950"
 

@@ -1,0 +1,531 @@
+// Exact attention backward (dQ, dK, dV) for MI355X / gfx950 (CDNA4).
+//
+// The gradients of O = softmax(s Q K^T) V for dL/dO = dO, per (batch, head) slice:
+//   P = exp(s Q K^T - LSE)   (rows; recomputed from the LSE the forward returned)
+//   dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P * (dP - D),
+//   dQ = s dS K,  dK = s dS^T Q.
+// "CUDA 算子工程：手写 FlashAttention v2 之路" ch. 14 §14.5 notes that the forward keeps
+// the LSE for this pass, and §14.7 that FA2's backward runs K/V-stationary (outer loop
+// over K/V blocks, inner over Q blocks) with dQ accumulated by atomics. Here dQ has a
+// kernel of its own instead, Q-stationary like the forward: both kernels recompute
+// P from the LSE, so no atomics, no fp32 dQ buffer, and the result is deterministic.
+//
+// Three launches on the caller's stream:
+//   1. fa_bwd_delta_kernel: D_i = dO_i . O_i (fp32, into the caller's workspace);
+//   2. fa_bwd_dq_kernel: a workgroup pins 128 query rows (4 waves x 32) with Q^T and
+//      dO^T in registers and streams K and V in tiles of 32 keys through LDS:
+//        S^T = K Q^T, dP^T = V dO^T            (MFMA, K and V rows from LDS)
+//        P^T = 2^(c S^T - LSE log2 e), dS^T = P^T * (dP^T - D)   (VALU)
+//        dQ^T += K^T dS^T                      (MFMA, K^T by transposing LDS reads)
+//   3. fa_bwd_dkdv_kernel: a workgroup pins 128 keys (4 waves x 32) with K^T and V^T
+//      in registers and streams Q, dO, LSE and D in tiles of 32 query rows:
+//        S = Q K^T, dP = dO V^T                (MFMA, Q and dO rows from LDS)
+//        P, dS as above, per query row          (VALU)
+//        dV^T += dO^T P, dK^T += Q^T dS        (MFMA, dO^T and Q^T by transposing reads)
+// Fragment layouts, LDS swizzle and the key/query permutation inside each 16-wide
+// MFMA step are those of the forward kernels.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <type_traits>
+
+#include "fa.h"
+#include "fa_device.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdParams {
+  const short* q;
+  const short* k;
+  const short* v;
+  const short* o;
+  const short* dout;
+  const float* lse;
+  float* delta;         // D = rowsum(dO * O), [slices][N]
+  short* dq;
+  short* dk;
+  short* dv;
+  int N;                // rows per slice (queries = keys)
+  int slices;           // B * H
+  uint32_t slice_bytes; // N * d * 2
+  int num_blocks;       // ceil(N / 128)
+  int total_wgs;        // slices * num_blocks
+  float c;              // scale * log2(e)
+  float scale;
+};
+
+template <bool BF16>
+__device__ __forceinline__ float to_f32(short x) {
+  if constexpr (BF16) return __builtin_bit_cast(float, (uint32_t)(uint16_t)x << 16);
+  else return (float)__builtin_bit_cast(_Float16, x);
+}
+
+// ---- 1. D_i = dO_i . O_i -------------------------------------------------------------
+// D / 8 lanes per row, 8 elements (16 bytes) each, then a butterfly sum.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const int64_t rows = (int64_t)p.slices * p.N;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int j = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const i16x8 a = *(const i16x8*)(p.dout + row * D + 8 * j);
+    const i16x8 b = *(const i16x8*)(p.o + row * D + 8 * j);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(to_f32<BF16>(a[e]), to_f32<BF16>(b[e]), acc);
+  }
+#pragma unroll
+  for (int w = LPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, LPR);
+  if (row < rows && j == 0) p.delta[row] = acc;
+}
+
+// Work item of a workgroup: slice and block of 128 rows (queries for dQ, keys for
+// dK/dV). Contiguous ranges per XCD, so the blocks of one slice share an L2.
+__device__ __forceinline__ void bwd_item(const BwdParams& p, int& bh, int& blk) {
+  const int bid = blockIdx.x;
+  const int T = p.total_wgs;
+  const int xcd = bid & 7, slot = bid >> 3, per = T >> 3, rem = T & 7;
+  const int w = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  bh = w / p.num_blocks;
+  blk = w - bh * p.num_blocks;
+}
+
+// Per-lane LDS element offsets of the fragment reads, for a tile of rows of D
+// elements stored with swz: rowf[ks] reads 8 elements of row l32, chunk 2 ks + hi
+// (an A operand row fragment); trf[db][sec] points the transposing read (see
+// ds_read_tr16) so that lane i of a 16-lane group gets four consecutive rows of one
+// column: together the A operand X^T with the row order of the B operands built
+// from an accumulator.
+template <int D>
+__device__ __forceinline__ void frag_offsets(int lane, int (&rowf)[D / 16], int (&trf)[D / 32][2]) {
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) rowf[ks] = l32 * D + (((2 * ks + hi) ^ swz<D>(l32)) << 3);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int r = 4 * hi + ((lane & 15) >> 2) + 8 * sec;
+      const int ch = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+      trf[db][sec] = r * D + ((ch ^ swz<D>(r)) << 3) + 4 * (lane & 1);
+    }
+}
+
+// Direct-to-LDS loads of a 32-row tile of D columns, split over 4 waves: load i of
+// the tile fills LDS bytes [1024 i, 1024 i + 1024); lane l writes tile row
+// ROWS i + 16 l / (2D), chunk position (16 l mod 2D) / 16, and so fetches chunk
+// position ^ swz(row) of the source row.
+template <int D>
+struct TileLoader {
+  static constexpr int LOADS = 32 * D * 2 / 1024;   // per tile
+  static constexpr int PER_WAVE = LOADS / 4;
+  static constexpr int ROWS = 1024 / (2 * D);       // tile rows per load
+  uint32_t off[PER_WAVE];
+  int wave;
+  __device__ __forceinline__ void init(int wave_, int lane) {
+    wave = wave_;
+#pragma unroll
+    for (int kk = 0; kk < PER_WAVE; ++kk) {
+      const int i = kk * 4 + wave;
+      const int r_local = (16 * lane) / (2 * D);
+      const int pch = ((16 * lane) % (2 * D)) / 16;
+      const int r = ROWS * (i % (16 / ROWS)) + r_local;
+      off[kk] = (uint32_t)((r_local * D + ((pch ^ swz<D>(r)) << 3)) * 2);
+    }
+  }
+  // rows row0 .. row0 + 31 of the slice behind rsrc into dst
+  __device__ __forceinline__ void issue(const __amdgpu_buffer_rsrc_t& rsrc, short* dst, int row0) const {
+#pragma unroll
+    for (int kk = 0; kk < PER_WAVE; ++kk) {
+      const int i = kk * 4 + wave;
+      buffer_load16_to_lds(rsrc, dst + 512 * i, off[kk], (uint32_t)((row0 + ROWS * i) * D * 2));
+    }
+  }
+};
+
+// 4 bytes per lane from memory into LDS: lane l writes [lds + 4 l, lds + 4 l + 4).
+__device__ __forceinline__ void buffer_load4_to_lds(__amdgpu_buffer_rsrc_t r, float* lds, uint32_t voff,
+                                                    uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) float*)lds), 4, voff, soff,
+      0, 0);
+}
+
+template <bool BF16>
+__device__ __forceinline__ i16x8 pack8(const float (&e)[8]) {
+  using f32x2 = float __attribute__((ext_vector_type(2)));
+  using e16x2 = typename std::conditional<BF16, __bf16 __attribute__((ext_vector_type(2))),
+                                          _Float16 __attribute__((ext_vector_type(2)))>::type;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  e16x2 h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = __builtin_convertvector((f32x2){e[2 * i], e[2 * i + 1]}, e16x2);
+  return __builtin_bit_cast(i16x8, ((u32x4){__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
+                                            __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])}));
+}
+
+// Store a transposed accumulator: acc[db][4 g + e] of lane (hi, l32) holds
+// X^T[d = 32 db + 8 g + 4 hi + e][row l32]; writes f * X[row][...] as 16-bit, 8 bytes per
+// store.
+template <int D, bool BF16>
+__device__ __forceinline__ void store_rows_t(short* row_ptr, int hi, const f32x16 (&acc)[D / 32], float f) {
+  using f32x2 = float __attribute__((ext_vector_type(2)));
+  using e16x2 = typename std::conditional<BF16, __bf16 __attribute__((ext_vector_type(2))),
+                                          _Float16 __attribute__((ext_vector_type(2)))>::type;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const e16x2 lo = __builtin_convertvector((f32x2){acc[db][4 * g] * f, acc[db][4 * g + 1] * f}, e16x2);
+      const e16x2 up = __builtin_convertvector((f32x2){acc[db][4 * g + 2] * f, acc[db][4 * g + 3] * f}, e16x2);
+      *(u32x2*)(row_ptr + db * 32 + 8 * g + 4 * hi) = (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, up)};
+    }
+}
+
+// ---- 2. dQ -----------------------------------------------------------------------------
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(BwdParams p) {
+#pragma clang fp contract(off)
+  constexpr int BM = 128, BN = 32, TILE = BN * D;
+  __shared__ __attribute__((aligned(1024))) short lds_k0[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_k1[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_v0[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_v1[TILE];
+
+  int bh, blk;
+  bwd_item(p, bh, blk);
+  if (CAUSAL) blk = p.num_blocks - 1 - blk;   // longest rows first
+  const int N = p.N;
+  const int m0 = blk * BM;
+  const int64_t base = (int64_t)bh * N * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, p.slice_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + base, p.slice_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base, p.slice_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base, p.slice_bytes);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wq0 = m0 + 32 * wave;
+  const int qrow = wq0 + l32;
+  const float c = p.c;
+
+  int rowf[D / 16], trf[D / 32][2];
+  frag_offsets<D>(lane, rowf, trf);
+  TileLoader<D> ld;
+  ld.init(wave, lane);
+
+  // Q^T and dO^T as B operands: 8 consecutive columns of this lane's query row
+  i16x8 qf[D / 16], dof[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    qf[ks] = buffer_load16(rq, (uint32_t)((qrow * D + ks * 16 + 8 * hi) * 2));
+    dof[ks] = buffer_load16(rdo, (uint32_t)((qrow * D + ks * 16 + 8 * hi) * 2));
+  }
+  // this lane's query: LSE in log2 units and D (rows past N: no weight)
+  const bool live = qrow < N;
+  const float lse2 = live ? p.lse[(int64_t)bh * N + qrow] * kLog2e : INFINITY;
+  const float dl = live ? p.delta[(int64_t)bh * N + qrow] : 0.f;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+  const int n_end = CAUSAL ? min(N, m0 + BM) : N;
+  const int ntiles = (n_end + BN - 1) / BN;
+  int n_full = (CAUSAL ? min(N, m0 + 1) : N) / BN;   // tiles visible to every query here
+  if (n_full > ntiles) n_full = ntiles;
+
+  auto sync_tile = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+  };
+
+  // One key tile: K rows in kbuf, V rows in vbuf (this iteration's stage).
+  auto step = [&](int n0, const short* kbuf, const short* vbuf, bool mask) __attribute__((always_inline)) {
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const i16x8 a = *(const i16x8*)(kbuf + rowf[ks]);
+      const i16x8 b = *(const i16x8*)(vbuf + rowf[ks]);
+      s = mfma_32x32x16<BF16>(a, qf[ks], s);
+      dp = mfma_32x32x16<BF16>(b, dof[ks], dp);
+    }
+    // s[r], dp[r]: key n0 + 8 (r / 4) + 4 hi + r % 4, query qrow
+    float ds[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+      if (mask) {
+        const int key = n0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (key >= N || (CAUSAL && key > qrow)) pr = 0.f;
+      }
+      ds[r] = pr * (dp[r] - dl);
+    }
+    i16x8 dsp[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = ds[8 * tt + i];
+      dsp[tt] = pack8<BF16>(e);
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const short* src = kbuf + 16 * tt * D;
+        const i16x4 a0 = ds_read_tr16(src + trf[db][0]);
+        const i16x4 a1 = ds_read_tr16(src + trf[db][1]);
+        acc[db] = mfma_32x32x16<BF16>(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), dsp[tt], acc[db]);
+      }
+  };
+
+  auto tile = [&](int j, short* k_rd, short* v_rd, short* k_wr, short* v_wr) __attribute__((always_inline)) {
+    sync_tile();
+    if (j + 1 < ntiles) {
+      ld.issue(rk, k_wr, (j + 1) * BN);
+      ld.issue(rv, v_wr, (j + 1) * BN);
+    }
+    const int n0 = j * BN;
+    if (CAUSAL && n0 > wq0 + 31) return;   // whole tile in this wave's future
+    step(n0, k_rd, v_rd, j >= n_full);
+  };
+  if (ntiles > 0) {
+    ld.issue(rk, lds_k0, 0);
+    ld.issue(rv, lds_v0, 0);
+  }
+  int j = 0;
+  for (; j + 1 < ntiles; j += 2) {
+    tile(j, lds_k0, lds_v0, lds_k1, lds_v1);
+    tile(j + 1, lds_k1, lds_v1, lds_k0, lds_v0);
+  }
+  if (j < ntiles) tile(j, lds_k0, lds_v0, lds_k1, lds_v1);
+
+  if (live) store_rows_t<D, BF16>(p.dq + base + (int64_t)qrow * D, hi, acc, p.scale);
+}
+
+// ---- 3. dK and dV --------------------------------------------------------------------
+// At d = 128 the K^T and V^T fragments and both accumulators need more than 256
+// registers, so that variant runs one wave per SIMD.
+template <int D, bool BF16, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void fa_bwd_dkdv_kernel(BwdParams p) {
+#pragma clang fp contract(off)
+  constexpr int BK = 128, BQ = 32, TILE = BQ * D;
+  __shared__ __attribute__((aligned(1024))) short lds_q0[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_q1[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_o0[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_o1[TILE];
+  __shared__ __attribute__((aligned(256))) float lds_l0[64];
+  __shared__ __attribute__((aligned(256))) float lds_l1[64];
+  __shared__ __attribute__((aligned(256))) float lds_d0[64];
+  __shared__ __attribute__((aligned(256))) float lds_d1[64];
+
+  int bh, blk;
+  bwd_item(p, bh, blk);
+  const int N = p.N;
+  const int n0 = blk * BK;                      // first key of this workgroup
+  const int64_t base = (int64_t)bh * N * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, p.slice_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + base, p.slice_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base, p.slice_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base, p.slice_bytes);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + (int64_t)bh * N, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.delta + (int64_t)bh * N, (uint32_t)N * 4);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int k0 = n0 + 32 * wave;                // this wave's first key
+  const int key = k0 + l32;                     // this lane's key (column of S, dP)
+  const float c = p.c;
+
+  int rowf[D / 16], trf[D / 32][2];
+  frag_offsets<D>(lane, rowf, trf);
+  TileLoader<D> ld;
+  ld.init(wave, lane);
+
+  // K^T and V^T as B operands: 8 consecutive columns of this lane's key row
+  i16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    kf[ks] = buffer_load16(rk, (uint32_t)((key * D + ks * 16 + 8 * hi) * 2));
+    vf[ks] = buffer_load16(rv, (uint32_t)((key * D + ks * 16 + 8 * hi) * 2));
+  }
+  f32x16 adk[D / 32], adv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { adk[db][r] = 0.f; adv[db][r] = 0.f; }
+
+  // query tiles: under a causal mask none before this workgroup's first key
+  const int T = (N + BQ - 1) / BQ;
+  const int t0 = CAUSAL ? n0 / BQ : 0;
+  const int t_wave = CAUSAL ? k0 / BQ : 0;      // first tile with a query that sees this wave's keys
+
+  auto issue = [&](int t, short* qd, short* od, float* lsd, float* dd) __attribute__((always_inline)) {
+    ld.issue(rq, qd, t * BQ);
+    ld.issue(rdo, od, t * BQ);
+    if (wave == 0) buffer_load4_to_lds(rl, lsd, (uint32_t)(4 * lane), (uint32_t)(t * BQ * 4));
+    if (wave == 1) buffer_load4_to_lds(rd, dd, (uint32_t)(4 * lane), (uint32_t)(t * BQ * 4));
+  };
+  auto sync_tile = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+  };
+
+  auto step = [&](int t, const short* qbuf, const short* obuf, const float* lsb, const float* db_, bool mask)
+      __attribute__((always_inline)) {
+    f32x16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const i16x8 a = *(const i16x8*)(qbuf + rowf[ks]);
+      const i16x8 b = *(const i16x8*)(obuf + rowf[ks]);
+      s = mfma_32x32x16<BF16>(a, kf[ks], s);
+      dp = mfma_32x32x16<BF16>(b, vf[ks], dp);
+    }
+    // s[r], dp[r]: query t BQ + 8 (r / 4) + 4 hi + r % 4, key `key`
+    float pr[16], ds[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      const f32x4 l4 = *(const f32x4*)(lsb + 8 * g + 4 * hi);
+      const f32x4 d4 = *(const f32x4*)(db_ + 8 * g + 4 * hi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -(l4[e] * kLog2e)));
+        if (mask) {
+          const int query = t * BQ + 8 * g + 4 * hi + e;
+          if (query >= N || (CAUSAL && key > query)) w = 0.f;
+        }
+        pr[r] = w;
+        ds[r] = w * (dp[r] - d4[e]);
+      }
+    }
+    i16x8 pp[2], dsp[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float e1[8], e2[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { e1[i] = pr[8 * tt + i]; e2[i] = ds[8 * tt + i]; }
+      pp[tt] = pack8<BF16>(e1);
+      dsp[tt] = pack8<BF16>(e2);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const i16x4 o0 = ds_read_tr16(obuf + 16 * tt * D + trf[db][0]);
+        const i16x4 o1 = ds_read_tr16(obuf + 16 * tt * D + trf[db][1]);
+        const i16x4 q0 = ds_read_tr16(qbuf + 16 * tt * D + trf[db][0]);
+        const i16x4 q1 = ds_read_tr16(qbuf + 16 * tt * D + trf[db][1]);
+        adv[db] = mfma_32x32x16<BF16>(__builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7), pp[tt], adv[db]);
+        adk[db] = mfma_32x32x16<BF16>(__builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7), dsp[tt], adk[db]);
+      }
+  };
+
+  auto tile = [&](int t, short* q_rd, short* o_rd, float* l_rd, float* d_rd, short* q_wr, short* o_wr, float* l_wr,
+                  float* d_wr) __attribute__((always_inline)) {
+    sync_tile();
+    if (t + 1 < T) issue(t + 1, q_wr, o_wr, l_wr, d_wr);
+    if (t < t_wave) return;                       // no query of this tile sees this wave's keys
+    const bool mask = (CAUSAL && t == t_wave) || (t + 1) * BQ > N;
+    step(t, q_rd, o_rd, l_rd, d_rd, mask);
+  };
+  if (t0 < T) issue(t0, lds_q0, lds_o0, lds_l0, lds_d0);
+  int t = t0;
+  for (; t + 1 < T; t += 2) {
+    tile(t, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
+    tile(t + 1, lds_q1, lds_o1, lds_l1, lds_d1, lds_q0, lds_o0, lds_l0, lds_d0);
+  }
+  if (t < T) tile(t, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
+
+  if (key < N) {
+    store_rows_t<D, BF16>(p.dk + base + (int64_t)key * D, hi, adk, p.scale);
+    store_rows_t<D, BF16>(p.dv + base + (int64_t)key * D, hi, adv, 1.f);
+  }
+}
+
+template <int D, bool BF16>
+hipError_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) {
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t rows = (int64_t)p.slices * p.N;
+  hipLaunchKernelGGL((fa_bwd_delta_kernel<D, BF16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+  if (causal) {
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, true>), dim3(p.total_wgs), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, true>), dim3(p.total_wgs), dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, false>), dim3(p.total_wgs), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, false>), dim3(p.total_wgs), dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return (size_t)(B * H * N) * 4;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                 fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_BAD_DTYPE;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_PTR;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv) & 15)
+    return FA_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
+  // one slice of a [B, H, N, d] tensor, plus the padded last block, in 32-bit byte offsets
+  if ((N + 512) * d * 2 >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
+  if (B * H >= ((int64_t)1 << 31) / ((N + 127) / 128 + 1)) return FA_ERR_TOO_LARGE;
+  if (B * H * N >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
+  if (!workspace || ((uintptr_t)workspace & 15) || workspace_bytes < (size_t)(B * H * N) * 4) return FA_ERR_WORKSPACE;
+  BwdParams p;
+  p.q = (const short*)q;
+  p.k = (const short*)k;
+  p.v = (const short*)v;
+  p.o = (const short*)o;
+  p.dout = (const short*)dout;
+  p.lse = lse;
+  p.delta = (float*)workspace;
+  p.dq = (short*)dq;
+  p.dk = (short*)dk;
+  p.dv = (short*)dv;
+  p.N = (int)N;
+  p.slices = (int)(B * H);
+  p.slice_bytes = (uint32_t)(N * d * 2);
+  p.num_blocks = (int)((N + 127) / 128);
+  p.total_wgs = p.slices * p.num_blocks;
+  p.c = (float)((double)scale * 1.4426950408889634);
+  p.scale = scale;
+  const hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dtype == FA_BF16;
+  hipError_t e;
+  if (d == 64) e = bf16 ? launch_bwd<64, true>(p, causal != 0, s) : launch_bwd<64, false>(p, causal != 0, s);
+  else e = bf16 ? launch_bwd<128, true>(p, causal != 0, s) : launch_bwd<128, false>(p, causal != 0, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -37,47 +37,9 @@
 #include <type_traits>
 
 #include "fa.h"
+#include "fa_device.h"
 
 namespace {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-
-constexpr float kLn2 = 0.6931471805599453f;
-
-template <bool BF16> struct Elem;
-template <> struct Elem<false> { using vec8 = f16x8; };
-template <> struct Elem<true> { using vec8 = bf16x8; };
-
-template <bool BF16>
-__device__ __forceinline__ f32x16 mfma_32x32x16(i16x8 a, i16x8 b, f32x16 c) {
-  using V = typename Elem<BF16>::vec8;
-  if constexpr (BF16)
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(V, a), __builtin_bit_cast(V, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(V, a), __builtin_bit_cast(V, b), c, 0, 0, 0);
-}
-
-// Reductions across the two 32-lane halves of a wave. v_permlane32_swap with the
-// same register as both operands leaves the low half's value in every lane of r[0]
-// and the high half's value in every lane of r[1].
-__device__ __forceinline__ float max_halves(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float sum_halves(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ i16x4 ds_read_tr16(const short* lds_ptr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) short*)lds_ptr));
-}
 
 // One launch: B batches of Hq query heads; query head h reads K/V head h / group.
 // Tensors are [B, heads, rows, d] with arbitrary batch/head/row strides (elements)
@@ -151,34 +113,6 @@ constexpr float kSumMax = 256.0f;
 // The P V MFMAs are issued at raised wave priority: the SIMD's other wave then gets
 // the VALU for its softmax while these MFMAs stream (measured: 5-20% faster).
 constexpr bool kRaisePvPriority = true;
-
-// Buffer resource over [base, base + bytes): loads at offsets past the end return
-// zeros, which pads the ragged last key/query tile without any branch.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ i16x8 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(i16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-// 16 bytes per lane straight from memory into LDS: lane l writes LDS bytes
-// [lds + 16 l, lds + 16 l + 16) (lds is wave-uniform); out-of-range lanes write zeros.
-__device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, short* lds, uint32_t voff,
-                                                     uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) short*)lds), 16, voff, soff,
-      0, 0);
-}
-
-// K and V tiles sit in LDS without padding, as rows of D 16-bit elements whose
-// 16-byte chunks are XOR-permuted per row: chunk c of row r is stored at chunk
-// position c ^ swz(r). For both the 32-row K fragment reads (16 lanes x 16 B) and the
-// transposing V reads (4 rows x 64 B per half wave) every access of a wave then
-// touches distinct banks. swz has period 16 in r.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  else return ((r & 3) << 2) | ((r >> 2) & 3);
-}
 
 // Epilogue of one wave: O = U / l and LSE = ln2 (ref + log2 l) for its QB blocks of 32
 // queries (l is split between the two lane halves), rounded into o and lse; or, for

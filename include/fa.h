@@ -48,7 +48,7 @@ typedef enum {
   FA_ERR_HIP = 9,                /* the HIP runtime reported an error at launch */
   FA_ERR_BAD_STRIDE = 10,        /* a stride is negative or not a multiple of 8 elements, or a row stride < d */
   FA_ERR_BAD_SPLITS = 11,        /* num_splits outside [1, 256] */
-  FA_ERR_WORKSPACE = 12          /* split-KV workspace NULL, not 16-byte aligned or too small */
+  FA_ERR_WORKSPACE = 12          /* workspace (split-KV or backward) NULL, not 16-byte aligned or too small */
 } fa_status;
 
 /*
@@ -169,6 +169,39 @@ size_t fa_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d, in
  * fa_fwd_ex (0, 0: the default tile). 1 when the query blocks alone fill the GPU. */
 int fa_split_default(int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, int causal,
                      int block_m, int block_n);
+
+/*
+ * fa_bwd — gradients of the attention forward, asynchronous on `stream`: for
+ * O = softmax(scale q k^T) v (fa_fwd's result, causal as there) and dout = dL/dO,
+ * writes dq = dL/dq, dk = dL/dk, dv = dL/dv. The pages define the forward; the
+ * forward's LSE output is kept for this pass ("CUDA 算子工程：手写 FlashAttention v2
+ * 之路" ch. 14 §14.5). The gradients are the forward differentiated:
+ * P = exp(scale q k^T - LSE) (recomputed from `lse`), dv = P^T dout,
+ * dP = dout v^T, D = rowsum(dout * o), dS = P * (dP - D), dq = scale dS k,
+ * dk = scale dS^T q.
+ *
+ *   q, k, v, o, dout: device pointers to [B, H, N, d] contiguous tensors of `dtype`
+ *             (o as returned by fa_fwd for these q, k, v, scale, causal). Read only.
+ *   lse     : [B, H, N] contiguous float32, as returned by fa_fwd.
+ *   dq, dk, dv: [B, H, N, d] contiguous `dtype`, fully overwritten; must not overlap
+ *             the inputs or each other.
+ *   workspace: device memory owned by the caller, 16-byte aligned, of at least
+ *             fa_bwd_workspace_bytes(B, H, N) bytes (the row sums D); contents on
+ *             entry do not matter; in use until the last kernel of the call has run.
+ *   B, H, N, d, scale, causal, dtype, stream: as for fa_fwd.
+ * Arithmetic: products in `dtype` on the matrix cores with fp32 accumulation; P and
+ * dS are rounded to `dtype` (round-to-nearest-even) before the products that use
+ * them. dq is computed by its own kernel (no atomics): results are deterministic.
+ * Errors as for fa_fwd, plus FA_ERR_WORKSPACE; B*H*N == 0 is a no-op.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                 int64_t d, float scale, int causal, fa_dtype dtype, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_bwd needs: 4 per query row (B * H * N * 4); 0 for an empty or
+ * negative size. */
+size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N);
 
 /* 1 if (block_m, block_n) is compiled for head dimension d, else 0. */
 int fa_tile_supported(int64_t d, int block_m, int block_n);

@@ -125,6 +125,23 @@ def test_split_sizes_and_default():
     assert fa.fa_split_default(1, 1, 1, 64, 0, 64, False) == 1
 
 
+def call_bwd(ptr=A, lse=A, ws=A, ws_bytes=1 << 20, B=1, H=2, N=100, d=64, scale=0.125, dtype=0):
+    return fa.fa_bwd(ptr, A, A, A, A, lse, A, A, A, B, H, N, d, scale, 0, dtype, ws, ws_bytes, None)
+
+
+def test_bwd_entry_validation_without_gpu():
+    assert call_bwd(B=-1) == 2 and call_bwd(N=-1) == 2
+    assert call_bwd(d=96) == 3
+    assert call_bwd(scale=0.0) == 4 and call_bwd(scale=float("nan")) == 4
+    assert call_bwd(dtype=7) == 5
+    assert call_bwd(ptr=None) == 1 and call_bwd(lse=None) == 1
+    assert call_bwd(ptr=A + 8) == 6 and call_bwd(lse=A + 2) == 6
+    assert call_bwd(ws=None) == 12 and call_bwd(ws_bytes=2 * 100 * 4 - 4) == 12 and call_bwd(ws=A + 4) == 12
+    assert call_bwd(N=1 << 24, d=128, ws_bytes=1 << 40) == 7
+    assert call_bwd(ptr=None, lse=None, ws=None, N=0) == 0
+    assert fa.fa_bwd_workspace_bytes(2, 3, 5) == 120 and fa.fa_bwd_workspace_bytes(0, 3, 5) == 0
+
+
 def test_empty_problems_need_no_pointers():
     assert call(q=None, k=None, v=None, o=None, lse=None, N=0) == 0
     assert call(q=None, k=None, v=None, o=None, lse=None, B=0) == 0

@@ -1,0 +1,123 @@
+"""GPU parity of the backward pass (fa_bwd, through the C ABI) against the fp64 CPU
+oracle's gradients on the very 16-bit inputs the GPU received.
+
+The contract is fa_fwd's: o and lse come from fa_fwd on the same q, k, v (the
+backward recomputes P from lse and uses o for the row sums D = dO . O).
+
+Tolerance (the target states none for gradients; derived from the arithmetic): per
+gradient tensor, max |G_gpu - G_oracle| <= 8 u max |G_oracle|, with u the dtype's
+unit roundoff (2^-11 fp16, 2^-8 bf16). Every product on the matrix cores has one
+16-bit operand that was rounded from fp32 just before (P for dV; dS for dQ and dK;
+each within u relative), O enters D rounded to the dtype, and the result is rounded
+once more: a handful of u relative to the largest terms, with fp32 accumulation far
+below that. The tests print the measured ratio.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_forward_fwd_amd as fa
+import oracle
+from exact_attention_forward_fwd_amd.workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+U = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+DEV = torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load_library()
+    yield
+
+
+def _rand(shape, dtype, seed):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn(shape, generator=g).to(TORCH_DT[dtype])
+
+
+def run_bwd(q, k, v, do, scale, causal, ws_fill=None):
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = fa.fwd(qd, kd, vd, scale=scale, causal=causal)
+    ws = None
+    if ws_fill is not None:
+        B, H, N, _ = q.shape
+        ws = torch.full((max(fa.fa_bwd_workspace_bytes(B, H, N), 16) // 4,), ws_fill, dtype=torch.float32, device=DEV)
+    dq, dk, dv = fa.bwd(qd, kd, vd, o, dod, lse, scale=scale, causal=causal, workspace=ws)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def check(q, k, v, do, scale, causal, dtype, label):
+    _say(f"[bwd] {label} shape={tuple(q.shape)} {dtype} causal={causal}")
+    got = run_bwd(q, k, v, do, scale, causal)
+    ref = oracle.attention_bwd(q.double().numpy(), k.double().numpy(), v.double().numpy(), do.double().numpy(),
+                               scale, causal)
+    ratios = []
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        gd = g.float().cpu().double().numpy()
+        assert np.all(np.isfinite(gd)), f"{label}: {name} not finite"
+        scale_r = np.abs(r).max()
+        err = np.abs(gd - r).max()
+        ratio = err / scale_r if scale_r > 0 else err
+        ratios.append(ratio)
+        assert ratio <= 8 * U[dtype], f"{label}: {name} max|d| / max|ref| = {ratio:.3e}"
+    _say(f"[bwd]   max|d|/max|ref|: dq {ratios[0]:.2e} dk {ratios[1]:.2e} dv {ratios[2]:.2e} (bound {8 * U[dtype]:.2e})")
+
+
+@pytest.mark.parametrize("n", [1, 17, 32, 64, 100, 129, 300, 513])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_sizes(n, d):
+    for dtype in ("f16", "bf16"):
+        for causal in (False, True):
+            seed = 7 * n + d + (1 if causal else 0)
+            q, k, v, do = (_rand((1, 2, n, d), dtype, seed + i) for i in range(4))
+            check(q, k, v, do, 1 / math.sqrt(d), causal, dtype, f"N={n} d={d}")
+
+
+@pytest.mark.parametrize("idx", [2, 3, 5])
+def test_bwd_workloads(idx):
+    """The forward benchmark workloads, with dO ~ N(0, 1) of the same shape: every
+    gradient element against the oracle."""
+    w = WORKLOADS[idx]
+    q, k, v, _ = make_inputs(w)
+    do = _rand(q.shape, w.dtype, 5000 + idx)
+    check(q, k, v, do, w.scale, w.causal, w.dtype, w.name)
+
+
+def test_bwd_deterministic_and_ignores_workspace_contents():
+    q, k, v, do = (_rand((2, 3, 700, 64), "f16", 90 + i) for i in range(4))
+    runs = [run_bwd(q, k, v, do, 0.125, True, ws_fill=f) for f in (0.0, float("nan"), 1e30)]
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b)
+
+
+def test_bwd_uniform_weights_closed_form():
+    """Q = 0 makes every valid key's weight 1/n_i: dV_j = sum_i dO_i / n_i over the rows
+    that see key j, and dK = 0 exactly."""
+    n, d = 200, 64
+    q = torch.zeros((1, 1, n, d), dtype=torch.float16)
+    k, v, do = (_rand((1, 1, n, d), "f16", 300 + i) for i in range(3))
+    for causal in (False, True):
+        dq, dk, dv = run_bwd(q, k, v, do, 0.125, causal)
+        dof = do[0, 0].double().numpy()
+        ev = np.zeros((n, d))
+        for i in range(n):
+            keys = np.arange(i + 1) if causal else np.arange(n)
+            ev[keys] += dof[i] / len(keys)
+        assert torch.count_nonzero(dk) == 0
+        err = np.abs(dv[0, 0].float().cpu().double().numpy() - ev).max() / np.abs(ev).max()
+        assert err <= 8 * U["f16"], err
