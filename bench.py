@@ -46,14 +46,18 @@ def parse():
 
 COPY_BYTES = 1 << 30   # 1 GiB read + 1 GiB written by the calibration copy
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(ROOT, "exact_attention_forward_fwd_amd", "csrc", "fa_fwd.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_forward_fwd_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_device.h")]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash() -> str:
+    """SHA-256 over the forward kernels' sources (the kernel file and the device helpers it includes)."""
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def algorithmic_bytes(w) -> int:
@@ -237,6 +241,82 @@ def time_split(w, steps, warmup):
     return rec
 
 
+def time_backward(w, steps, warmup):
+    """Per-call device time of fa_bwd (row sums, dQ kernel, dK/dV kernel) on a forward
+    benchmark workload with dO ~ N(0, 1), o and lse from fa_fwd. Algorithmic FLOPs are
+    the five products of the gradient (S, dP, dV, dK, dQ: 2.5x the forward's); the
+    kernels execute seven (S and dP once more in the dQ kernel)."""
+    import torch
+    import exact_attention_forward_fwd_amd as fa
+    from exact_attention_forward_fwd_amd.workloads import make_inputs
+
+    dev = torch.device("cuda:0")
+    q, k, v, _ = make_inputs(w)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    g = torch.Generator("cpu").manual_seed(5000 + w.index)
+    do = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
+    o, lse = fa.fwd(q, k, v, scale=w.scale, causal=w.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    lib = fa.load_library()
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), w.B, w.H, w.N, w.d, float(w.scale), int(w.causal),
+            fa.FA_F16 if w.dtype == "f16" else fa.FA_BF16, ws.data_ptr(), ws.numel(), stream.cuda_stream)
+
+    def call():
+        rc = lib.fa_bwd(*args)
+        if rc != 0:
+            raise fa.FaError(rc, "fa_bwd")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    avg = sum(per) / len(per)
+    alg = 2.5 * w.flops
+    tf = alg / (avg * 1e-3) / 1e12
+    return {"workload": w.name, "dtype": w.dtype, "causal": w.causal, "call_ms_avg": round(avg, 5),
+            "call_ms_median": round(per[len(per) // 2], 5),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "algorithmic_flop": alg,
+                         "executed_flop": 3.5 * w.flops}}
+
+
+def cpu_baseline_backward(w, budget_s=6.0):
+    """The fp64 oracle's backward on whole (b, h) slices of the workload until the budget
+    is spent (at least one slice), priced at the same algorithmic FLOPs."""
+    import oracle
+    from exact_attention_forward_fwd_amd.workloads import make_inputs
+
+    q, k, v, _ = make_inputs(w)
+    q = q.double().numpy().reshape(-1, w.N, w.d)
+    k = k.double().numpy().reshape(-1, w.N, w.d)
+    v = v.double().numpy().reshape(-1, w.N, w.d)
+    import numpy as np
+    do = np.random.default_rng(5000 + w.index).standard_normal(q.shape)
+    slices = 0
+    t0 = time.perf_counter()
+    while slices < q.shape[0]:
+        n = min(16, q.shape[0] - slices)   # one slice per thread
+        oracle.attention_bwd(q[slices:slices + n], k[slices:slices + n], v[slices:slices + n],
+                             do[slices:slices + n], w.scale, w.causal)
+        slices += n
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    alg = 2.5 * w.flops / (w.B * w.H) * slices
+    return {"value": alg / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{slices} of {w.B * w.H} (batch, head) slices of {w.label()}, every gradient, fp64 C "
+                      f"oracle backward, {dt:.1f} s"}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The fp64 oracle on this workload's inputs: whole (b, h) slices, in order, until
     the budget is spent (at least one slice)."""
@@ -336,6 +416,11 @@ def main():
         out["split_kv"] = [time_split(ws, max(10, args.steps // 2), max(3, args.warmup // 2))
                            for ws in SPLIT_WORKLOADS.values()]
         torch.cuda.empty_cache()
+        out["backward"] = [time_backward(WORKLOADS[i], max(5, args.steps // 5), max(2, args.warmup // 2))
+                           for i in (2, 4, 3)]
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            out["backward"][0]["cpu_baseline"] = cpu_baseline_backward(WORKLOADS[2])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
