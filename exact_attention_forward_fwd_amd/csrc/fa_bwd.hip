@@ -18,7 +18,8 @@
 //        P^T = 2^(c S^T - LSE log2 e), dS^T = P^T * (dP^T - D)   (VALU)
 //        dQ^T += K^T dS^T                      (MFMA, K^T by transposing LDS reads)
 //   3. fa_bwd_dkdv_kernel: a workgroup pins 128 keys (4 waves x 32) with K^T and V^T
-//      in registers and streams Q, dO, LSE and D in tiles of 32 query rows:
+//      in registers (V in LDS for non-causal d = 128) and streams Q, dO, LSE and D
+//      in tiles of 32 query rows:
 //        S = Q K^T, dP = dO V^T                (MFMA, Q and dO rows from LDS)
 //        P, dS as above, per query row          (VALU)
 //        dV^T += dO^T P, dK^T += Q^T dS        (MFMA, dO^T and Q^T by transposing reads)
@@ -316,12 +317,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 }
 
 // ---- 3. dK and dV --------------------------------------------------------------------
-// At d = 128 the K^T and V^T fragments and both accumulators need more than 256
-// registers, so that variant runs one wave per SIMD.
+// At d = 128, K^T and V^T fragments in registers plus both accumulators need more
+// than 256 registers. Without a causal mask the workgroup's V rows stay in LDS
+// (32 KB) and the V^T fragments are read per tile, which keeps two waves per SIMD
+// (measured 24% faster despite a few spills in the loop); with the mask's extra
+// registers that variant spills more and is slower than one wave per SIMD with
+// everything in registers (measured), which the causal kernel therefore keeps.
 template <int D, bool BF16, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void fa_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 128 && CAUSAL) ? 1 : 2))) void fa_bwd_dkdv_kernel(BwdParams p) {
 #pragma clang fp contract(off)
   constexpr int BK = 128, BQ = 32, TILE = BQ * D;
+  constexpr bool V_LDS = (D == 128 && !CAUSAL);
+  __shared__ __attribute__((aligned(1024))) short lds_vk[V_LDS ? BK * D : 8];
   __shared__ __attribute__((aligned(1024))) short lds_q0[TILE];
   __shared__ __attribute__((aligned(1024))) short lds_q1[TILE];
   __shared__ __attribute__((aligned(1024))) short lds_o0[TILE];
@@ -355,13 +362,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
   TileLoader<D> ld;
   ld.init(wave, lane);
 
-  // K^T and V^T as B operands: 8 consecutive columns of this lane's key row
-  i16x8 kf[D / 16], vf[D / 16];
+  // K^T and V^T as B operands: 8 consecutive columns of this lane's key row (V^T
+  // from LDS per tile when V_LDS)
+  i16x8 kf[D / 16], vf[V_LDS ? 1 : D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    kf[ks] = buffer_load16(rk, (uint32_t)((key * D + ks * 16 + 8 * hi) * 2));
-    vf[ks] = buffer_load16(rv, (uint32_t)((key * D + ks * 16 + 8 * hi) * 2));
+  for (int ks = 0; ks < D / 16; ++ks) kf[ks] = buffer_load16(rk, (uint32_t)((key * D + ks * 16 + 8 * hi) * 2));
+  if constexpr (V_LDS) {
+#pragma unroll
+    for (int b = 0; b < BK / BQ; ++b) ld.issue(rv, lds_vk + b * BQ * D, n0 + b * BQ);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) vf[ks] = buffer_load16(rv, (uint32_t)((key * D + ks * 16 + 8 * hi) * 2));
   }
+  const short* vrows = lds_vk + 32 * wave * D;   // this wave's 32 V rows (V_LDS)
   f32x16 adk[D / 32], adv[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -390,37 +403,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) s = mfma_32x32x16<BF16>(*(const i16x8*)(qbuf + rowf[ks]), kf[ks], s);
+#pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const i16x8 a = *(const i16x8*)(qbuf + rowf[ks]);
       const i16x8 b = *(const i16x8*)(obuf + rowf[ks]);
-      s = mfma_32x32x16<BF16>(a, kf[ks], s);
-      dp = mfma_32x32x16<BF16>(b, vf[ks], dp);
+      i16x8 vk;
+      if constexpr (V_LDS) vk = *(const i16x8*)(vrows + rowf[ks]);
+      else vk = vf[ks];
+      dp = mfma_32x32x16<BF16>(b, vk, dp);
     }
-    // s[r], dp[r]: query t BQ + 8 (r / 4) + 4 hi + r % 4, key `key`
-    float pr[16], ds[16];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      typedef float f32x4 __attribute__((ext_vector_type(4)));
-      const f32x4 l4 = *(const f32x4*)(lsb + 8 * g + 4 * hi);
-      const f32x4 d4 = *(const f32x4*)(db_ + 8 * g + 4 * hi);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -(l4[e] * kLog2e)));
-        if (mask) {
-          const int query = t * BQ + 8 * g + 4 * hi + e;
-          if (query >= N || (CAUSAL && key > query)) w = 0.f;
-        }
-        pr[r] = w;
-        ds[r] = w * (dp[r] - d4[e]);
-      }
-    }
+    // s[r], dp[r]: query t BQ + 8 (r / 4) + 4 hi + r % 4, key `key`. Each half (8
+    // rows) is rounded and packed as soon as it is computed.
     i16x8 pp[2], dsp[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       float e1[8], e2[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) { e1[i] = pr[8 * tt + i]; e2[i] = ds[8 * tt + i]; }
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * tt + gg;
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 l4 = *(const f32x4*)(lsb + 8 * g + 4 * hi);
+        const f32x4 d4 = *(const f32x4*)(db_ + 8 * g + 4 * hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -(l4[e] * kLog2e)));
+          if (mask) {
+            const int query = t * BQ + 8 * g + 4 * hi + e;
+            if (query >= N || (CAUSAL && key > query)) w = 0.f;
+          }
+          e1[4 * gg + e] = w;
+          e2[4 * gg + e] = w * (dp[r] - d4[e]);
+        }
+      }
       pp[tt] = pack8<BF16>(e1);
       dsp[tt] = pack8<BF16>(e2);
     }
