@@ -22,7 +22,7 @@ STATUS_NAMES = {
     12: "FA_ERR_WORKSPACE",
 }
 EXPORTED = ("fa_fwd", "fa_fwd_tiled", "fa_fwd_ex", "fa_fwd_split", "fa_split_workspace_bytes", "fa_split_default",
-            "fa_bwd", "fa_bwd_workspace_bytes", "fa_tile_supported", "fa_default_tile", "fa_status_str")
+            "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "fa_tile_supported", "fa_default_tile", "fa_status_str")
 
 
 class FaError(RuntimeError):
@@ -63,6 +63,9 @@ def load_library(path: str = LIB_PATH):
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp,
                            ctypes.c_size_t, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float, i32,
+                              i32, vp, ctypes.c_size_t, vp]
+    lib.fa_bwd_ex.restype = i32
     lib.fa_bwd_workspace_bytes.argtypes = [i64, i64, i64]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_tile_supported.argtypes = [i64, i32, i32]
@@ -128,6 +131,13 @@ def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, dtype, 
     """Raw C call of the backward entry point; pointers are device addresses."""
     return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, int(causal), dtype,
                                  workspace, int(workspace_bytes), stream)
+
+
+def fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hk, Nq, Nk, d, scale, causal, dtype, workspace,
+              workspace_bytes, stream) -> int:
+    """Raw C call of the general backward entry point."""
+    return load_library().fa_bwd_ex(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hk, Nq, Nk, d, scale, int(causal),
+                                    dtype, workspace, int(workspace_bytes), stream)
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
@@ -306,4 +316,39 @@ def bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = False,
                 workspace.data_ptr(), workspace.numel() * workspace.element_size(), sp)
     if st != 0:
         raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def bwd_ex(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = False, dq=None, dk=None, dv=None,
+           workspace=None, stream=None):
+    """Gradients for ``fwd_ex`` with contiguous tensors: q, o, dout [B, Hq, Nq, d]; k, v
+    [B, Hk, Nk, d]; lse [B, Hq, Nq] (o and lse from fwd_ex on the same inputs). Returns
+    (dq, dk, dv); dk and dv of a K/V head sum over the query heads that share it."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor of q's dtype")
+    B, Hq, Nq, d = q.shape
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must be shaped like q")
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must be [B, Hk, Nk, d] with q's B and d")
+    Hk, Nk = k.shape[1], k.shape[2]
+    if not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(max(fa_bwd_workspace_bytes(B, Hq, Nq), 16), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hk, Nq, Nk, d, float(scale), causal,
+                   _dtype_code(q), workspace.data_ptr(), workspace.numel() * workspace.element_size(), sp)
+    if st != 0:
+        raise FaError(st, "fa_bwd_ex")
     return dq, dk, dv

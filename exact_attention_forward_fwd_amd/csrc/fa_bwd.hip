@@ -44,15 +44,19 @@ struct BwdParams {
   const short* o;
   const short* dout;
   const float* lse;
-  float* delta;         // D = rowsum(dO * O), [slices][N]
+  float* delta;         // D = rowsum(dO * O), [slices_q][Nq]
   short* dq;
   short* dk;
   short* dv;
-  int N;                // rows per slice (queries = keys)
-  int slices;           // B * H
-  uint32_t slice_bytes; // N * d * 2
-  int num_blocks;       // ceil(N / 128)
-  int total_wgs;        // slices * num_blocks
+  int Nq, Nk;           // query rows, key rows per slice
+  int Hq, group;        // query heads; query heads per K/V head (head h reads K/V head h / group)
+  int off;              // causal: key j is visible to query i iff j <= i + off (off = Nk - Nq)
+  int slices_q;         // B * Hq (q, o, dout, dq, lse, D are [B, Hq, Nq, ...])
+  uint32_t q_bytes;     // Nq * d * 2: one query slice
+  uint32_t k_bytes;     // Nk * d * 2: one K/V slice
+  int qblocks, kblocks; // ceil(Nq / 128), ceil(Nk / 128)
+  int dq_wgs;           // slices_q * qblocks
+  int dkdv_wgs;         // B * Hk * kblocks
   float c;              // scale * log2(e)
   float scale;
 };
@@ -69,7 +73,7 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdParams p) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;
-  const int64_t rows = (int64_t)p.slices * p.N;
+  const int64_t rows = (int64_t)p.slices_q * p.Nq;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int j = threadIdx.x % LPR;
   float acc = 0.f;
@@ -84,16 +88,18 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdParams p) {
   if (row < rows && j == 0) p.delta[row] = acc;
 }
 
-// Work item of a workgroup: slice and block of 128 rows (queries for dQ, keys for
-// dK/dV). Contiguous ranges per XCD, so the blocks of one slice share an L2.
-__device__ __forceinline__ void bwd_item(const BwdParams& p, int& bh, int& blk) {
+// Work item of a workgroup out of T: slice and block of 128 rows (queries for dQ,
+// keys for dK/dV). Contiguous ranges per XCD, so the blocks of one slice share an L2.
+__device__ __forceinline__ void bwd_item(int T, int nblocks, int& bh, int& blk) {
   const int bid = blockIdx.x;
-  const int T = p.total_wgs;
   const int xcd = bid & 7, slot = bid >> 3, per = T >> 3, rem = T & 7;
   const int w = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-  bh = w / p.num_blocks;
-  blk = w - bh * p.num_blocks;
+  bh = w / nblocks;
+  blk = w - bh * nblocks;
 }
+
+// floor(a / b) for b > 0 and any sign of a
+__device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
 
 // Per-lane LDS element offsets of the fragment reads, for a tile of rows of D
 // elements stored with swz: rowf[ks] reads 8 elements of row l32, chunk 2 ks + hi
@@ -199,15 +205,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   __shared__ __attribute__((aligned(1024))) short lds_v1[TILE];
 
   int bh, blk;
-  bwd_item(p, bh, blk);
-  if (CAUSAL) blk = p.num_blocks - 1 - blk;   // longest rows first
-  const int N = p.N;
+  bwd_item(p.dq_wgs, p.qblocks, bh, blk);
+  if (CAUSAL) blk = p.qblocks - 1 - blk;   // longest rows first
+  const int Nq = p.Nq, Nk = p.Nk, off = p.off;
   const int m0 = blk * BM;
-  const int64_t base = (int64_t)bh * N * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, p.slice_bytes);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + base, p.slice_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base, p.slice_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base, p.slice_bytes);
+  const int b = bh / p.Hq, h = bh - b * p.Hq;
+  const int64_t base = (int64_t)bh * Nq * D;                                       // query slice
+  const int64_t base_k = ((int64_t)b * (p.Hq / p.group) + h / p.group) * Nk * D;  // its K/V slice
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + base, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base_k, p.k_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base_k, p.k_bytes);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -228,10 +236,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     qf[ks] = buffer_load16(rq, (uint32_t)((qrow * D + ks * 16 + 8 * hi) * 2));
     dof[ks] = buffer_load16(rdo, (uint32_t)((qrow * D + ks * 16 + 8 * hi) * 2));
   }
-  // this lane's query: LSE in log2 units and D (rows past N: no weight)
-  const bool live = qrow < N;
-  const float lse2 = live ? p.lse[(int64_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dl = live ? p.delta[(int64_t)bh * N + qrow] : 0.f;
+  // this lane's query: LSE in log2 units and D (rows past Nq, or seeing no key at
+  // all, LSE = -inf: no weight)
+  const bool live = qrow < Nq;
+  const float lse_raw = live ? p.lse[(int64_t)bh * Nq + qrow] : -INFINITY;
+  const float lse2 = lse_raw == -INFINITY ? INFINITY : lse_raw * kLog2e;
+  const float dl = live ? p.delta[(int64_t)bh * Nq + qrow] : 0.f;
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -239,9 +249,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-  const int n_end = CAUSAL ? min(N, m0 + BM) : N;
+  const int n_end = CAUSAL ? max(0, min(Nk, m0 + BM + off)) : Nk;
   const int ntiles = (n_end + BN - 1) / BN;
-  int n_full = (CAUSAL ? min(N, m0 + 1) : N) / BN;   // tiles visible to every query here
+  int n_full = (CAUSAL ? max(0, min(Nk, m0 + 1 + off)) : Nk) / BN;   // tiles visible to every query here
   if (n_full > ntiles) n_full = ntiles;
 
   auto sync_tile = [&]() {
@@ -268,7 +278,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
       float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
       if (mask) {
         const int key = n0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (key >= N || (CAUSAL && key > qrow)) pr = 0.f;
+        if (key >= Nk || (CAUSAL && key > qrow + off)) pr = 0.f;
       }
       ds[r] = pr * (dp[r] - dl);
     }
@@ -299,7 +309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
       ld.issue(rv, v_wr, (j + 1) * BN);
     }
     const int n0 = j * BN;
-    if (CAUSAL && n0 > wq0 + 31) return;   // whole tile in this wave's future
+    if (CAUSAL && n0 > wq0 + 31 + off) return;   // whole tile in this wave's future
     step(n0, k_rd, v_rd, j >= n_full);
   };
   if (ntiles > 0) {
@@ -338,23 +348,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 128 &
   __shared__ __attribute__((aligned(256))) float lds_d0[64];
   __shared__ __attribute__((aligned(256))) float lds_d1[64];
 
-  int bh, blk;
-  bwd_item(p, bh, blk);
-  const int N = p.N;
+  int bhk, blk;                                 // K/V slice (batch, K/V head) and key block
+  bwd_item(p.dkdv_wgs, p.kblocks, bhk, blk);
+  const int Nq = p.Nq, Nk = p.Nk, off = p.off, group = p.group;
+  const int hk_count = p.Hq / group;
+  const int b = bhk / hk_count, kh = bhk - b * hk_count;
   const int n0 = blk * BK;                      // first key of this workgroup
-  const int64_t base = (int64_t)bh * N * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, p.slice_bytes);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + base, p.slice_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base, p.slice_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base, p.slice_bytes);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + (int64_t)bh * N, (uint32_t)N * 4);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.delta + (int64_t)bh * N, (uint32_t)N * 4);
+  const int64_t base = (int64_t)bhk * Nk * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base, p.k_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base, p.k_bytes);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int k0 = n0 + 32 * wave;                // this wave's first key
   const int key = k0 + l32;                     // this lane's key (column of S, dP)
+  const int key_rel = key - off;                // visible to query i iff key_rel <= i
   const float c = p.c;
 
   int rowf[D / 16], trf[D / 32][2];
@@ -381,16 +390,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 128 &
 #pragma unroll
     for (int r = 0; r < 16; ++r) { adk[db][r] = 0.f; adv[db][r] = 0.f; }
 
-  // query tiles: under a causal mask none before this workgroup's first key
-  const int T = (N + BQ - 1) / BQ;
-  const int t0 = CAUSAL ? n0 / BQ : 0;
-  const int t_wave = CAUSAL ? k0 / BQ : 0;      // first tile with a query that sees this wave's keys
+  // Query tiles of 32 rows, for each of the group's query heads in turn. Under a
+  // causal mask a tile matters once its
+  // last query sees a key of this workgroup (32 t + 31 + off >= n0), and for a wave
+  // once it sees one of the wave's keys; the wave's tiles up to the one whose first
+  // query sees its last key need the mask.
+  const int T = (Nq + BQ - 1) / BQ;
+  const int t0 = CAUSAL ? max(0, -floor_div(off + 31 - n0, BQ)) : 0;
+  const int t_wave = CAUSAL ? max(0, -floor_div(off + 31 - k0, BQ)) : 0;
+  const int t_nomask = CAUSAL ? -floor_div(off - 31 - k0, BQ) : 0;    // tiles from here need no causal mask
 
+  // buffer descriptors of the query head being processed
+  __amdgpu_buffer_rsrc_t rq, rdo, rls, rdl;
+  auto set_head = [&](int g) __attribute__((always_inline)) {
+    const int64_t bq = (int64_t)b * p.Hq + kh * group + g;   // query slice
+    rq = make_rsrc(p.q + bq * Nq * D, p.q_bytes);
+    rdo = make_rsrc(p.dout + bq * Nq * D, p.q_bytes);
+    rls = make_rsrc(p.lse + bq * Nq, (uint32_t)Nq * 4);
+    rdl = make_rsrc(p.delta + bq * Nq, (uint32_t)Nq * 4);
+  };
   auto issue = [&](int t, short* qd, short* od, float* lsd, float* dd) __attribute__((always_inline)) {
     ld.issue(rq, qd, t * BQ);
     ld.issue(rdo, od, t * BQ);
-    if (wave == 0) buffer_load4_to_lds(rl, lsd, (uint32_t)(4 * lane), (uint32_t)(t * BQ * 4));
-    if (wave == 1) buffer_load4_to_lds(rd, dd, (uint32_t)(4 * lane), (uint32_t)(t * BQ * 4));
+    if (wave == 0) buffer_load4_to_lds(rls, lsd, (uint32_t)(4 * lane), (uint32_t)(t * BQ * 4));
+    if (wave == 1) buffer_load4_to_lds(rdl, dd, (uint32_t)(4 * lane), (uint32_t)(t * BQ * 4));
   };
   auto sync_tile = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -399,16 +422,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 128 &
 
   auto step = [&](int t, const short* qbuf, const short* obuf, const float* lsb, const float* db_, bool mask)
       __attribute__((always_inline)) {
+    // With V in LDS the registers are the scarce resource, not the vector ALU: the
+    // fragment offsets are recomputed per tile from the lane index (one XOR-shift
+    // each) instead of staying live across the loop.
+    int rfv[D / 16], tfv[D / 32][2];
+    if constexpr (V_LDS) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      frag_offsets<D>(ln, rfv, tfv);
+    }
+    const int(&rf)[D / 16] = V_LDS ? rfv : rowf;
+    const int(&tf)[D / 32][2] = V_LDS ? tfv : trf;
     f32x16 s, dp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) s = mfma_32x32x16<BF16>(*(const i16x8*)(qbuf + rowf[ks]), kf[ks], s);
+    for (int ks = 0; ks < D / 16; ++ks) s = mfma_32x32x16<BF16>(*(const i16x8*)(qbuf + rf[ks]), kf[ks], s);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const i16x8 b = *(const i16x8*)(obuf + rowf[ks]);
+      const i16x8 b = *(const i16x8*)(obuf + rf[ks]);
       i16x8 vk;
-      if constexpr (V_LDS) vk = *(const i16x8*)(vrows + rowf[ks]);
+      if constexpr (V_LDS) vk = *(const i16x8*)(vrows + rf[ks]);
       else vk = vf[ks];
       dp = mfma_32x32x16<BF16>(b, vk, dp);
     }
@@ -430,7 +464,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 128 &
           float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -(l4[e] * kLog2e)));
           if (mask) {
             const int query = t * BQ + 8 * g + 4 * hi + e;
-            if (query >= N || (CAUSAL && key > query)) w = 0.f;
+            if (query >= Nq || (CAUSAL && key_rel > query)) w = 0.f;
           }
           e1[4 * gg + e] = w;
           e2[4 * gg + e] = w * (dp[r] - d4[e]);
@@ -444,10 +478,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 128 &
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const i16x4 o0 = ds_read_tr16(obuf + 16 * tt * D + trf[db][0]);
-        const i16x4 o1 = ds_read_tr16(obuf + 16 * tt * D + trf[db][1]);
-        const i16x4 q0 = ds_read_tr16(qbuf + 16 * tt * D + trf[db][0]);
-        const i16x4 q1 = ds_read_tr16(qbuf + 16 * tt * D + trf[db][1]);
+        const i16x4 o0 = ds_read_tr16(obuf + 16 * tt * D + tf[db][0]);
+        const i16x4 o1 = ds_read_tr16(obuf + 16 * tt * D + tf[db][1]);
+        const i16x4 q0 = ds_read_tr16(qbuf + 16 * tt * D + tf[db][0]);
+        const i16x4 q1 = ds_read_tr16(qbuf + 16 * tt * D + tf[db][1]);
         adv[db] = mfma_32x32x16<BF16>(__builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7), pp[tt], adv[db]);
         adk[db] = mfma_32x32x16<BF16>(__builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7), dsp[tt], adk[db]);
       }
@@ -458,18 +492,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 128 &
     sync_tile();
     if (t + 1 < T) issue(t + 1, q_wr, o_wr, l_wr, d_wr);
     if (t < t_wave) return;                       // no query of this tile sees this wave's keys
-    const bool mask = (CAUSAL && t == t_wave) || (t + 1) * BQ > N;
+    const bool mask = (CAUSAL && t < t_nomask) || (t + 1) * BQ > Nq;
     step(t, q_rd, o_rd, l_rd, d_rd, mask);
   };
-  if (t0 < T) issue(t0, lds_q0, lds_o0, lds_l0, lds_d0);
-  int t = t0;
-  for (; t + 1 < T; t += 2) {
-    tile(t, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
-    tile(t + 1, lds_q1, lds_o1, lds_l1, lds_d1, lds_q0, lds_o0, lds_l0, lds_d0);
+  // The query heads that share this K/V head, one after the other (one head without
+  // grouping). Loads are double-buffered within a head; a new head starts once every
+  // wave is done with the previous head's last tile.
+  for (int g = 0; g < group; ++g) {
+    if (g > 0) __syncthreads();
+    set_head(g);
+    if (t0 < T) issue(t0, lds_q0, lds_o0, lds_l0, lds_d0);
+    int t = t0;
+    for (; t + 1 < T; t += 2) {
+      tile(t, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
+      tile(t + 1, lds_q1, lds_o1, lds_l1, lds_d1, lds_q0, lds_o0, lds_l0, lds_d0);
+    }
+    if (t < T) tile(t, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
   }
-  if (t < T) tile(t, lds_q0, lds_o0, lds_l0, lds_d0, lds_q1, lds_o1, lds_l1, lds_d1);
 
-  if (key < N) {
+  if (key < Nk) {
     store_rows_t<D, BF16>(p.dk + base + (int64_t)key * D, hi, adk, p.scale);
     store_rows_t<D, BF16>(p.dv + base + (int64_t)key * D, hi, adv, 1.f);
   }
@@ -478,16 +519,75 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((D == 128 &
 template <int D, bool BF16>
 hipError_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) {
   constexpr int RPB = 256 / (D / 8);
-  const int64_t rows = (int64_t)p.slices * p.N;
-  hipLaunchKernelGGL((fa_bwd_delta_kernel<D, BF16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+  const int64_t rows = (int64_t)p.slices_q * p.Nq;
+  if (rows > 0)
+    hipLaunchKernelGGL((fa_bwd_delta_kernel<D, BF16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
   if (causal) {
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, true>), dim3(p.total_wgs), dim3(256), 0, s, p);
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, true>), dim3(p.total_wgs), dim3(256), 0, s, p);
+    if (p.dq_wgs > 0) hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, true>), dim3(p.dq_wgs), dim3(256), 0, s, p);
+    if (p.dkdv_wgs > 0) hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, true>), dim3(p.dkdv_wgs), dim3(256), 0, s, p);
   } else {
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, false>), dim3(p.total_wgs), dim3(256), 0, s, p);
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, false>), dim3(p.total_wgs), dim3(256), 0, s, p);
+    if (p.dq_wgs > 0) hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, false>), dim3(p.dq_wgs), dim3(256), 0, s, p);
+    if (p.dkdv_wgs > 0) hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, false>), dim3(p.dkdv_wgs), dim3(256), 0, s, p);
   }
   return hipGetLastError();
+}
+
+// Shared by fa_bwd and fa_bwd_ex: contiguous [B, H, N, d] tensors, K/V heads shared by
+// Hq / Hk query heads, Nq queries against Nk keys (causal: bottom-right alignment).
+fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d,
+                  float scale, int causal, fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || Hq < 0 || Hk < 0 || Nq < 0 || Nk < 0) return FA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_BAD_DTYPE;
+  if (B == 0 || (Hq == 0 && Hk == 0)) return FA_OK;
+  if (Hq == 0 || Hk == 0 || Hq % Hk != 0) return FA_ERR_BAD_SHAPE;
+  if (Nq == 0 && Nk == 0) return FA_OK;
+  const bool has_q = Nq > 0, has_k = Nk > 0;
+  if ((has_q && (!q || !o || !dout || !lse || !dq)) || (has_k && (!k || !v || !dk || !dv))) return FA_ERR_NULL_PTR;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv) & 15)
+    return FA_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
+  // one slice plus the padded last block in 32-bit byte offsets; grid and row counts in int
+  if ((Nq + 512) * d * 2 >= ((int64_t)1 << 31) || (Nk + 512) * d * 2 >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
+  const int64_t qblocks = (Nq + 127) / 128, kblocks = (Nk + 127) / 128;
+  if (B * Hq >= ((int64_t)1 << 31) / (qblocks + kblocks + 1)) return FA_ERR_TOO_LARGE;
+  if (B * Hq * Nq >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
+  if (has_q && (!workspace || ((uintptr_t)workspace & 15) || workspace_bytes < (size_t)(B * Hq * Nq) * 4))
+    return FA_ERR_WORKSPACE;
+  BwdParams p;
+  p.q = (const short*)q;
+  p.k = (const short*)k;
+  p.v = (const short*)v;
+  p.o = (const short*)o;
+  p.dout = (const short*)dout;
+  p.lse = lse;
+  p.delta = (float*)workspace;
+  p.dq = (short*)dq;
+  p.dk = (short*)dk;
+  p.dv = (short*)dv;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.Hq = (int)Hq;
+  p.group = (int)(Hq / Hk);
+  p.off = (int)(Nk - Nq);
+  p.slices_q = (int)(B * Hq);
+  p.q_bytes = (uint32_t)(Nq * d * 2);
+  p.k_bytes = (uint32_t)(Nk * d * 2);
+  p.qblocks = (int)qblocks;
+  p.kblocks = (int)kblocks;
+  p.dq_wgs = (int)(B * Hq * qblocks);
+  p.dkdv_wgs = (int)(B * Hk * kblocks);
+  p.c = (float)((double)scale * 1.4426950408889634);
+  p.scale = scale;
+  const hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dtype == FA_BF16;
+  hipError_t e;
+  if (d == 64) e = bf16 ? launch_bwd<64, true>(p, causal != 0, s) : launch_bwd<64, false>(p, causal != 0, s);
+  else e = bf16 ? launch_bwd<128, true>(p, causal != 0, s) : launch_bwd<128, false>(p, causal != 0, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // namespace
@@ -502,45 +602,16 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                  void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
                  fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 0 || H < 0 || N < 0) return FA_ERR_BAD_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
-  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_BAD_SCALE;
-  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_BAD_DTYPE;
-  if (B == 0 || H == 0 || N == 0) return FA_OK;
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_PTR;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout | (uintptr_t)dq |
-       (uintptr_t)dk | (uintptr_t)dv) & 15)
-    return FA_ERR_MISALIGNED;
-  if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
-  // one slice of a [B, H, N, d] tensor, plus the padded last block, in 32-bit byte offsets
-  if ((N + 512) * d * 2 >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
-  if (B * H >= ((int64_t)1 << 31) / ((N + 127) / 128 + 1)) return FA_ERR_TOO_LARGE;
-  if (B * H * N >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
-  if (!workspace || ((uintptr_t)workspace & 15) || workspace_bytes < (size_t)(B * H * N) * 4) return FA_ERR_WORKSPACE;
-  BwdParams p;
-  p.q = (const short*)q;
-  p.k = (const short*)k;
-  p.v = (const short*)v;
-  p.o = (const short*)o;
-  p.dout = (const short*)dout;
-  p.lse = lse;
-  p.delta = (float*)workspace;
-  p.dq = (short*)dq;
-  p.dk = (short*)dk;
-  p.dv = (short*)dv;
-  p.N = (int)N;
-  p.slices = (int)(B * H);
-  p.slice_bytes = (uint32_t)(N * d * 2);
-  p.num_blocks = (int)((N + 127) / 128);
-  p.total_wgs = p.slices * p.num_blocks;
-  p.c = (float)((double)scale * 1.4426950408889634);
-  p.scale = scale;
-  const hipStream_t s = (hipStream_t)stream;
-  const bool bf16 = dtype == FA_BF16;
-  hipError_t e;
-  if (d == 64) e = bf16 ? launch_bwd<64, true>(p, causal != 0, s) : launch_bwd<64, false>(p, causal != 0, s);
-  else e = bf16 ? launch_bwd<128, true>(p, causal != 0, s) : launch_bwd<128, false>(p, causal != 0, s);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, N, d, scale, causal, dtype, workspace,
+                 workspace_bytes, stream);
+}
+
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk,
+                    int64_t d, float scale, int causal, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hk, Nq, Nk, d, scale, causal, dtype, workspace,
+                 workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -199,8 +199,23 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int64_t d, float scale, int causal, fa_dtype dtype, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/*
+ * fa_bwd_ex — fa_bwd for grouped K/V heads and unequal lengths, as fa_fwd_ex computes
+ * them: q, o, dout, dq are [B, Hq, Nq, d], k, v, dk, dv are [B, Hk, Nk, d] (contiguous),
+ * lse [B, Hq, Nq]; query head h reads K/V head h / (Hq / Hk), so dk and dv of a K/V
+ * head sum the contributions of its Hq / Hk query heads; causal masks key
+ * j > i + Nk - Nq (bottom-right). o and lse come from fa_fwd_ex on the same inputs.
+ * Rows that see no key get dq = 0. The workspace holds 4 bytes per query row:
+ * fa_bwd_workspace_bytes(B, Hq, Nq). Other arguments and errors as for fa_bwd; Nq = 0
+ * writes dk = dv = 0, Nk = 0 writes dq = 0.
+ */
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hk,
+                    int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, fa_dtype dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes fa_bwd needs: 4 per query row (B * H * N * 4); 0 for an empty or
- * negative size. */
+ * negative size. For fa_bwd_ex pass H = Hq and N = Nq. */
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N);
 
 /* 1 if (block_m, block_n) is compiled for head dimension d, else 0. */

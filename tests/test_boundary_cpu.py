@@ -142,6 +142,18 @@ def test_bwd_entry_validation_without_gpu():
     assert fa.fa_bwd_workspace_bytes(2, 3, 5) == 120 and fa.fa_bwd_workspace_bytes(0, 3, 5) == 0
 
 
+def call_bwd_ex(ptr=A, ws=A, ws_bytes=1 << 20, B=1, Hq=4, Hk=2, Nq=100, Nk=70, d=64):
+    return fa.fa_bwd_ex(ptr, A, A, A, A, A, A, A, A, B, Hq, Hk, Nq, Nk, d, 0.125, 1, 0, ws, ws_bytes, None)
+
+
+def test_bwd_ex_validation_without_gpu():
+    assert call_bwd_ex(Hk=3) == 2 and call_bwd_ex(Hk=0) == 2 and call_bwd_ex(Nk=-1) == 2
+    assert call_bwd_ex(ptr=None) == 1
+    assert call_bwd_ex(ws=None) == 12 and call_bwd_ex(ws_bytes=4 * 100 * 4 - 4) == 12
+    assert call_bwd_ex(ptr=None, ws=None, Nq=0, Nk=0) == 0
+    assert call_bwd_ex(ptr=None, ws=None, B=0) == 0
+
+
 def test_empty_problems_need_no_pointers():
     assert call(q=None, k=None, v=None, o=None, lse=None, N=0) == 0
     assert call(q=None, k=None, v=None, o=None, lse=None, B=0) == 0

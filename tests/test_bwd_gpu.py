@@ -121,3 +121,77 @@ def test_bwd_uniform_weights_closed_form():
         assert torch.count_nonzero(dk) == 0
         err = np.abs(dv[0, 0].float().cpu().double().numpy() - ev).max() / np.abs(ev).max()
         assert err <= 8 * U["f16"], err
+
+
+def check_ex(B, hq, hk, nq, nk, d, dtype, causal, seed, label):
+    """fa_bwd_ex against the oracle on K/V repeated per query head (the definition of
+    the grouping); the gradient of a shared K/V head is the sum over its query heads."""
+    _say(f"[bwd_ex] {label} hq={hq} hk={hk} nq={nq} nk={nk} d={d} {dtype} causal={causal}")
+    q, do = _rand((B, hq, nq, d), dtype, seed), _rand((B, hq, nq, d), dtype, seed + 3)
+    k, v = _rand((B, hk, nk, d), dtype, seed + 1), _rand((B, hk, nk, d), dtype, seed + 2)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = fa.fwd_ex(qd, kd, vd, scale=1 / math.sqrt(d), causal=causal)
+    dq, dk, dv = fa.bwd_ex(qd, kd, vd, o, dod, lse, scale=1 / math.sqrt(d), causal=causal)
+    torch.cuda.synchronize()
+    g = hq // hk
+    rq, rk, rv = oracle.attention_bwd(q.double().numpy(), k.repeat_interleave(g, dim=1).double().numpy(),
+                                      v.repeat_interleave(g, dim=1).double().numpy(), do.double().numpy(),
+                                      1 / math.sqrt(d), causal, align="bottom-right")
+    rk = rk.reshape(B, hk, g, nk, d).sum(axis=2)
+    rv = rv.reshape(B, hk, g, nk, d).sum(axis=2)
+    ratios = []
+    for name, gg, r in zip(("dq", "dk", "dv"), (dq, dk, dv), (rq, rk, rv)):
+        gd = gg.float().cpu().double().numpy()
+        assert np.all(np.isfinite(gd)), f"{label}: {name} not finite"
+        m = np.abs(r).max() if r.size else 0.0
+        err = np.abs(gd - r).max() if r.size else 0.0
+        ratio = err / m if m > 0 else err
+        ratios.append(ratio)
+        assert ratio <= 8 * U[dtype], f"{label}: {name} max|d| / max|ref| = {ratio:.3e}"
+    if causal and nq > nk:   # rows that see no key
+        assert torch.count_nonzero(dq[:, :, : nq - nk]) == 0
+    _say(f"[bwd_ex]   max|d|/max|ref|: dq {ratios[0]:.2e} dk {ratios[1]:.2e} dv {ratios[2]:.2e}")
+
+
+@pytest.mark.parametrize("hq,hk", [(8, 2), (4, 1), (6, 3)])
+def test_bwd_grouped_kv_heads(hq, hk):
+    for d, dtype in ((64, "f16"), (128, "bf16")):
+        for causal in (False, True):
+            check_ex(2, hq, hk, 300, 300, d, dtype, causal, seed=hq * 7 + hk + d, label="gqa")
+
+
+@pytest.mark.parametrize("nq,nk", [(1, 300), (37, 515), (300, 100), (100, 1), (64, 1000), (513, 129), (129, 513)])
+def test_bwd_unequal_lengths(nq, nk):
+    for d, dtype in ((64, "f16"), (128, "bf16")):
+        for causal in (False, True):
+            check_ex(1, 4, 2, nq, nk, d, dtype, causal, seed=nq + 3 * nk + d, label="lengths")
+
+
+def test_bwd_no_keys_and_no_queries():
+    for d in (64, 128):
+        q = _rand((1, 2, 50, d), "f16", 1).to(DEV)
+        kz = torch.zeros((1, 2, 0, d), dtype=torch.float16, device=DEV)
+        o, lse = fa.fwd_ex(q, kz, kz, causal=False)
+        dq, dk, dv = fa.bwd_ex(q, kz, kz, o, q.clone(), lse)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(dq) == 0 and dk.numel() == 0
+        # no queries: dk = dv = 0 for every key
+        qz = torch.zeros((1, 2, 0, d), dtype=torch.float16, device=DEV)
+        k = _rand((1, 2, 70, d), "f16", 2).to(DEV)
+        oz, lz = fa.fwd_ex(qz, k, k, causal=True)
+        dk0 = torch.full_like(k, float("nan"))
+        dv0 = torch.full_like(k, float("nan"))
+        fa.bwd_ex(qz, k, k, oz, qz, lz, causal=True, dk=dk0, dv=dv0)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(dk0) == 0 and torch.count_nonzero(dv0) == 0
+
+
+def test_bwd_ex_equals_bwd_when_plain():
+    q, k, v, do = (_rand((2, 3, 333, 128), "bf16", 40 + i).to(DEV) for i in range(4))
+    for causal in (False, True):
+        o, lse = fa.fwd(q, k, v, causal=causal)
+        a = fa.bwd(q, k, v, o, do, lse, causal=causal)
+        b = fa.bwd_ex(q, k, v, o, do, lse, causal=causal)
+        torch.cuda.synchronize()
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
