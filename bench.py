@@ -141,6 +141,36 @@ def profile_mode(w, launches=3):
     print(json.dumps({"profile": w.name, "launches": launches, "copy_bytes": COPY_BYTES}), flush=True)
 
 
+def time_calls(call, stream, steps):
+    """Device time of `call` on `stream`. The timed region is `steps` back-to-back calls
+    between one pair of HIP events recorded on that stream: its length / steps is the
+    average. A second pass brackets every call with its own events for the median and
+    minimum; an event between calls leaves a gap of a few microseconds, so that pass
+    does not give the average."""
+    import torch
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(steps):
+        call()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    total_ms = t0.elapsed_time(t1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    return dict(avg=total_ms / steps, total=total_ms, median=per[len(per) // 2], min=per[0],
+                wall_ms=(wall1 - wall0) * 1e3)
+
+
 def time_workload(w, steps, warmup):
     import torch
     import exact_attention_forward_fwd_amd as fa
@@ -160,28 +190,10 @@ def time_workload(w, steps, warmup):
 
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    # events bracket every launch on the kernel's own stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    t_all0 = torch.cuda.Event(enable_timing=True)
-    t_all1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_all0.record(stream)
-    for i in range(steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-    t_all1.record(stream)
-    torch.cuda.synchronize()
-    wall1 = time.perf_counter()
-    per = sorted(a.elapsed_time(b) for a, b in ev)
-    total_ms = t_all0.elapsed_time(t_all1)
-    return dict(ms_per_step=total_ms / steps, kernel_ms_avg=sum(per) / len(per),
-                kernel_ms_median=per[len(per) // 2], kernel_ms_min=per[0],
-                wall_ms_per_step=(wall1 - wall0) * 1e3 / steps,
-                inputs=(q, k, v))
+    # one launch per step: the step time is the kernel's average launch duration
+    t = time_calls(step, stream, steps)
+    return dict(ms_per_step=t["avg"], kernel_ms_avg=t["avg"], kernel_ms_median=t["median"],
+                kernel_ms_min=t["min"], wall_ms_per_step=t["wall_ms"] / steps, inputs=(q, k, v))
 
 
 def time_split(w, steps, warmup):
@@ -213,15 +225,8 @@ def time_split(w, steps, warmup):
                 raise fa.FaError(rc, "fa_fwd_split")
         for _ in range(warmup):
             call()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for i in range(steps):
-            ev[i][0].record(stream)
-            call()
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        per = sorted(a.elapsed_time(b) for a, b in ev)
-        return sum(per) / len(per), per[len(per) // 2]
+        t = time_calls(call, stream, steps)
+        return t["avg"], t["median"]
 
     avg, med = run(splits)
     avg1, _ = run(1)
@@ -271,19 +276,12 @@ def time_backward(w, steps, warmup):
 
     for _ in range(warmup):
         call()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record(stream)
-        call()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    per = sorted(a.elapsed_time(b) for a, b in ev)
-    avg = sum(per) / len(per)
+    t = time_calls(call, stream, steps)
+    avg = t["avg"]
     alg = 2.5 * w.flops
     tf = alg / (avg * 1e-3) / 1e12
     return {"workload": w.name, "dtype": w.dtype, "causal": w.causal, "call_ms_avg": round(avg, 5),
-            "call_ms_median": round(per[len(per) // 2], 5),
+            "call_ms_median": round(t["median"], 5),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / MFMA_PEAK_TFLOPS, 4), "algorithmic_flop": alg,
                          "executed_flop": 3.5 * w.flops}}
