@@ -229,24 +229,42 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   const int wq0 = m0 + wave * 32 * QB;     // first query of this wave
   const float c = p.c;
 
-  // ---- per-lane LDS offsets (elements), fixed for the whole loop ----
+  // ---- per-lane LDS offsets (elements) ----
   // K fragment (A operand of S^T = K Q^T): row 32 kb + l32, 16-byte chunk 2 ks + hi.
-  int koff[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = l32 * D + (((2 * ks + hi) ^ swz<D>(l32)) << 3);
   // V^T fragment via ds_read_b64_tr_b16. Lane (group of 16 = g, index i) receives
   // element j from lane 4j + i/4 of its group, component i%4. With lane L of the
   // group pointing at V[key0 + L/4][dcol0 + 4 (L%4)], lane i gets V[key0 + j][dcol0 + i],
   // j = 0..3: four consecutive keys of one d column. Second read: keys key0 + 8...
-  int voff[D / 32][2];
+  auto frag_offsets = [](int ln, int (&ko)[D / 16], int (&vo)[D / 32][2]) __attribute__((always_inline)) {
+    const int r32 = ln & 31, h = ln >> 5;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int ks = 0; ks < D / 16; ++ks) ko[ks] = r32 * D + (((2 * ks + h) ^ swz<D>(r32)) << 3);
 #pragma unroll
-    for (int sec = 0; sec < 2; ++sec) {
-      const int r = 4 * hi + ((lane & 15) >> 2) + 8 * sec;          // row within a 16-row period
-      const int ch = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-      voff[db][sec] = r * D + ((ch ^ swz<D>(r)) << 3) + 4 * (lane & 1);
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        const int r = 4 * h + ((ln & 15) >> 2) + 8 * sec;          // row within a 16-row period
+        const int ch = 4 * db + 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
+        vo[db][sec] = r * D + ((ch ^ swz<D>(r)) << 3) + 4 * (ln & 1);
+      }
+  };
+  // The offsets normally stay in registers for the whole loop. In the two d = 128
+  // variants whose loop otherwise spills (causal with 64-key tiles, non-causal with
+  // 32-key tiles; the accumulators, Q^T and the previous tile's weights take most
+  // of 256 registers) they are recomputed where they are used (one XOR and shift
+  // each) from a copy of the lane index the compiler cannot hoist out of the loop.
+  // Measured: 449 -> 775 and 878 -> 1075 TFLOP/s; the other variants do not spill
+  // in their loop and only lose by the extra VALU work.
+  constexpr bool RECOMPUTE_OFFSETS = D == 128 && ((CAUSAL && BN == 64) || (!CAUSAL && BN == 32));
+  int koff_live[D / 16], voff_live[D / 32][2];
+  frag_offsets(lane, koff_live, voff_live);
+  auto fresh_offsets = [&](int (&ko)[D / 16], int (&vo)[D / 32][2]) __attribute__((always_inline)) {
+    if constexpr (RECOMPUTE_OFFSETS) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      frag_offsets(ln, ko, vo);
     }
+  };
   // Direct-to-LDS loads: load i of a tile fills LDS bytes [1024 i, 1024 i + 1024),
   // i.e. rows ROWS_PER_DMA*i.. of the tile; lane l fills tile row
   // ROWS_PER_DMA*i + 16 l / (2D), chunk position p = (16 l mod 2D) / 16, and so fetches
@@ -308,6 +326,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   if (n_full > ntiles) n_full = ntiles;
 
   auto pv = [&](const short* vbuf) {
+    int ko_new[D / 16], vo_new[D / 32][2];
+    fresh_offsets(ko_new, vo_new);
+    const int(&koff)[D / 16] = RECOMPUTE_OFFSETS ? ko_new : koff_live;
+    const int(&voff)[D / 32][2] = RECOMPUTE_OFFSETS ? vo_new : voff_live;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -329,6 +351,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     constexpr bool HAVE_PREV = decltype(prev_tag)::value;
     // ---- S^T = K_tile Q^T: each K fragment feeds QB MFMAs ----
     constexpr bool PRIO_ALL = kRaisePvPriority && D == 64;
+    int ko_new[D / 16], vo_new[D / 32][2];
+    fresh_offsets(ko_new, vo_new);
+    const int(&koff)[D / 16] = RECOMPUTE_OFFSETS ? ko_new : koff_live;
+    const int(&voff)[D / 32][2] = RECOMPUTE_OFFSETS ? vo_new : voff_live;
     f32x16 s[QB][BN / 32];
     if constexpr (PRIO_ALL) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
@@ -1004,20 +1030,17 @@ fa_status read_strides(const int64_t* st, int64_t H, int64_t N, int64_t d, int64
 void default_tile(int64_t N, int64_t d, int causal, int* bm, int* bn) {
   // Measured on MI355X (interleaved tile sweeps per workload family):
   //  - short sequences: the smallest tile, so that more workgroups exist;
-  //  - causal, and d = 64: the four-wave kernel with one 32-query block per wave
-  //    (causal row blocks of uneven length balance better with small blocks);
-  //    64-key tiles for long non-causal d = 64, 32-key tiles otherwise;
-  //  - long non-causal d = 128: the eight-wave kernel (one wave of each SIMD pair
-  //    issues MFMAs while the other runs its softmax), 32-key tiles.
+  //  - the four-wave kernel with one 32-query block per wave otherwise (causal row
+  //    blocks of uneven length balance better with small blocks): 64-key tiles
+  //    for long non-causal sequences (d = 64 and d = 128), 32-key tiles otherwise.
+  //    At d = 128 the non-causal 64-key tile beats the eight-wave kernel
+  //    (1252 against 1191 TFLOP/s at N = 16384, 1143 against 990 at N = 4096).
   if (N <= 128) {
     *bm = 64;
     *bn = 64;
-  } else if (causal || d == 64 || N <= 256) {
-    *bm = 128;
-    *bn = (d == 64 && !causal && N > 256) ? 64 : 32;
   } else {
-    *bm = 256;
-    *bn = 32;
+    *bm = 128;
+    *bn = (!causal && N > 256) ? 64 : 32;
   }
 }
 
