@@ -11,16 +11,19 @@
 // P from the LSE, so no atomics, no fp32 dQ buffer, and the result is deterministic.
 //
 // Three launches on the caller's stream:
-//   1. fa_bwd_delta_kernel: D_i = dO_i . O_i (fp32, into the caller's workspace);
+//   1. fa_bwd_delta_kernel: -D_i = -dO_i . O_i and the LSE in base-2 units
+//      (LSE_i log2 e, +inf for a row that sees no key), fp32, into the caller's
+//      workspace;
 //   2. fa_bwd_dq_kernel: a workgroup pins 128 query rows (4 waves x 32) with Q^T and
 //      dO^T in registers and streams K and V in tiles of 32 keys through LDS:
 //        S^T = K Q^T, dP^T = V dO^T            (MFMA, K and V rows from LDS)
 //        P^T = 2^(c S^T - LSE log2 e), dS^T = P^T * (dP^T - D)   (VALU)
 //        dQ^T += K^T dS^T                      (MFMA, K^T by transposing LDS reads)
 //   3. fa_bwd_dkdv_kernel: a workgroup pins 128 keys (4 waves x 32) with K^T and V^T
-//      in registers (V in LDS for non-causal d = 128) and streams Q, dO, LSE and D
-//      in tiles of 32 query rows:
-//        S = Q K^T, dP = dO V^T                (MFMA, Q and dO rows from LDS)
+//      in registers (V in LDS at d = 128) and streams Q, dO, LSE and -D in tiles of
+//      32 query rows:
+//        S = Q K^T, dP - D = dO V^T - D        (MFMA, Q and dO rows from LDS; the
+//                                               accumulator starts from -D)
 //        P, dS as above, per query row          (VALU)
 //        dV^T += dO^T P, dK^T += Q^T dS        (MFMA, dO^T and Q^T by transposing reads)
 // Fragment layouts, LDS swizzle and the key/query permutation inside each 16-wide
@@ -44,7 +47,8 @@ struct BwdParams {
   const short* o;
   const short* dout;
   const float* lse;
-  float* delta;         // D = rowsum(dO * O), [slices_q][Nq]
+  float* nd;            // -D = -rowsum(dO * O), [slices_q][Nq] (workspace)
+  float* l2;            // LSE in log2 units, +inf for a row that sees no key, [slices_q][Nq] (workspace)
   short* dq;
   short* dk;
   short* dv;
@@ -85,7 +89,11 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdParams p) {
   }
 #pragma unroll
   for (int w = LPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, LPR);
-  if (row < rows && j == 0) p.delta[row] = acc;
+  if (row < rows && j == 0) {
+    p.nd[row] = -acc;
+    const float lse = p.lse[row];
+    p.l2[row] = lse == -INFINITY ? INFINITY : lse * kLog2e;
+  }
 }
 
 // Work item of a workgroup out of T: slice and block of 128 rows (queries for dQ,
@@ -237,11 +245,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     dof[ks] = buffer_load16(rdo, (uint32_t)((qrow * D + ks * 16 + 8 * hi) * 2));
   }
   // this lane's query: LSE in log2 units and D (rows past Nq, or seeing no key at
-  // all, LSE = -inf: no weight)
+  // all: +inf, no weight)
   const bool live = qrow < Nq;
-  const float lse_raw = live ? p.lse[(int64_t)bh * Nq + qrow] : -INFINITY;
-  const float lse2 = lse_raw == -INFINITY ? INFINITY : lse_raw * kLog2e;
-  const float dl = live ? p.delta[(int64_t)bh * Nq + qrow] : 0.f;
+  const float lse2 = live ? p.l2[(int64_t)bh * Nq + qrow] : INFINITY;
+  const float dl = live ? -p.nd[(int64_t)bh * Nq + qrow] : 0.f;
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -417,8 +424,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t bq = (int64_t)b * p.Hq + kh * group + g;   // query slice
     rq = make_rsrc(p.q + bq * Nq * D, p.q_bytes);
     rdo = make_rsrc(p.dout + bq * Nq * D, p.q_bytes);
-    rls = make_rsrc(p.lse + bq * Nq, (uint32_t)Nq * 4);
-    rdl = make_rsrc(p.delta + bq * Nq, (uint32_t)Nq * 4);
+    rls = make_rsrc(p.l2 + bq * Nq, (uint32_t)Nq * 4);
+    rdl = make_rsrc(p.nd + bq * Nq, (uint32_t)Nq * 4);
   };
   auto issue = [&](int t, short* qd, short* od, float* lsd, float* dd) __attribute__((always_inline)) {
     ld.issue(rq, qd, t * BQ);
@@ -447,9 +454,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     const int(&rf)[D / 16] = V_LDS ? rfv : rowf;
     const int(&tf)[D / 32][2] = V_LDS ? tfv : trf;
+    // dP starts from -D of its query rows, so the products land as dP - D
     f32x16 s, dp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
+    for (int g = 0; g < 4; ++g) {
+      typedef float f32x4 __attribute__((ext_vector_type(4)));
+      const f32x4 nd4 = *(const f32x4*)(db_ + 8 * g + 4 * hi);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { s[4 * g + e] = 0.f; dp[4 * g + e] = nd4[e]; }
+    }
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) s = mfma_32x32x16<BF16>(*(const i16x8*)(qbuf + rf[ks]), kf[ks], s);
 #pragma unroll
@@ -471,17 +484,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int g = 2 * tt + gg;
         typedef float f32x4 __attribute__((ext_vector_type(4)));
         const f32x4 l4 = *(const f32x4*)(lsb + 8 * g + 4 * hi);
-        const f32x4 d4 = *(const f32x4*)(db_ + 8 * g + 4 * hi);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -(l4[e] * kLog2e)));
+          float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l4[e]));
           if (mask) {
             const int query = t * BQ + 8 * g + 4 * hi + e;
             if (query >= Nq || (CAUSAL && key_rel > query)) w = 0.f;
           }
           e1[4 * gg + e] = w;
-          e2[4 * gg + e] = w * (dp[r] - d4[e]);
+          e2[4 * gg + e] = w * dp[r];
         }
       }
       pp[tt] = pack8<BF16>(e1);
@@ -574,7 +586,7 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   const int64_t qblocks = (Nq + 127) / 128, kblocks = (Nk + 127) / 128;
   if (B * Hq >= ((int64_t)1 << 31) / (qblocks + kblocks + 1)) return FA_ERR_TOO_LARGE;
   if (B * Hq * Nq >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
-  if (has_q && (!workspace || ((uintptr_t)workspace & 15) || workspace_bytes < (size_t)(B * Hq * Nq) * 4))
+  if (has_q && (!workspace || ((uintptr_t)workspace & 15) || workspace_bytes < (size_t)(B * Hq * Nq) * 8))
     return FA_ERR_WORKSPACE;
   BwdParams p;
   p.q = (const short*)q;
@@ -583,7 +595,8 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   p.o = (const short*)o;
   p.dout = (const short*)dout;
   p.lse = lse;
-  p.delta = (float*)workspace;
+  p.nd = (float*)workspace;
+  p.l2 = (float*)workspace + B * Hq * Nq;
   p.dq = (short*)dq;
   p.dk = (short*)dk;
   p.dv = (short*)dv;
@@ -615,7 +628,7 @@ extern "C" {
 
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return (size_t)(B * H * N) * 4;
+  return (size_t)(B * H * N) * 8;
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

@@ -186,8 +186,9 @@ int fa_split_default(int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, 
  *   dq, dk, dv: [B, H, N, d] contiguous `dtype`, fully overwritten; must not overlap
  *             the inputs or each other.
  *   workspace: device memory owned by the caller, 16-byte aligned, of at least
- *             fa_bwd_workspace_bytes(B, H, N) bytes (the row sums D); contents on
- *             entry do not matter; in use until the last kernel of the call has run.
+ *             fa_bwd_workspace_bytes(B, H, N) bytes (per query row: -D and the LSE
+ *             in base-2 units); contents on entry do not matter; in use until the
+ *             last kernel of the call has run.
  *   B, H, N, d, scale, causal, dtype, stream: as for fa_fwd.
  * Arithmetic: products in `dtype` on the matrix cores with fp32 accumulation; P and
  * dS are rounded to `dtype` (round-to-nearest-even) before the products that use
@@ -205,7 +206,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
  * lse [B, Hq, Nq]; query head h reads K/V head h / (Hq / Hk), so dk and dv of a K/V
  * head sum the contributions of its Hq / Hk query heads; causal masks key
  * j > i + Nk - Nq (bottom-right). o and lse come from fa_fwd_ex on the same inputs.
- * Rows that see no key get dq = 0. The workspace holds 4 bytes per query row:
+ * Rows that see no key get dq = 0. The workspace holds 8 bytes per query row:
  * fa_bwd_workspace_bytes(B, Hq, Nq). Other arguments and errors as for fa_bwd; Nq = 0
  * writes dk = dv = 0, Nk = 0 writes dq = 0.
  */
@@ -214,7 +215,7 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
                     int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, fa_dtype dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes fa_bwd needs: 4 per query row (B * H * N * 4); 0 for an empty or
+/* Workspace bytes fa_bwd needs: 8 per query row (B * H * N * 8); 0 for an empty or
  * negative size. For fa_bwd_ex pass H = Hq and N = Nq. */
 size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N);
 

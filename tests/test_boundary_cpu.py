@@ -139,7 +139,7 @@ def test_bwd_entry_validation_without_gpu():
     assert call_bwd(ws=None) == 12 and call_bwd(ws_bytes=2 * 100 * 4 - 4) == 12 and call_bwd(ws=A + 4) == 12
     assert call_bwd(N=1 << 24, d=128, ws_bytes=1 << 40) == 7
     assert call_bwd(ptr=None, lse=None, ws=None, N=0) == 0
-    assert fa.fa_bwd_workspace_bytes(2, 3, 5) == 120 and fa.fa_bwd_workspace_bytes(0, 3, 5) == 0
+    assert fa.fa_bwd_workspace_bytes(2, 3, 5) == 240 and fa.fa_bwd_workspace_bytes(0, 3, 5) == 0
 
 
 def call_bwd_ex(ptr=A, ws=A, ws_bytes=1 << 20, B=1, Hq=4, Hk=2, Nq=100, Nk=70, d=64):
