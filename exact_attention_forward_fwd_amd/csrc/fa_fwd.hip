@@ -254,16 +254,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   // of 256 registers) they are recomputed where they are used (one XOR and shift
   // each) from a copy of the lane index the compiler cannot hoist out of the loop.
   // Measured: 449 -> 775 and 878 -> 1075 TFLOP/s; the other variants do not spill
-  // in their loop and only lose by the extra VALU work.
+  // in their main loop and only lose by the extra VALU work. The non-causal 64-key
+  // variant recomputes them in its masked tiles (the ragged last tile) only, where
+  // the mask's registers made it spill (N = 1000, B = 8, H = 32: 683 -> 825 TFLOP/s).
   constexpr bool RECOMPUTE_OFFSETS = D == 128 && ((CAUSAL && BN == 64) || (!CAUSAL && BN == 32));
+  constexpr bool RECOMPUTE_MASKED = RECOMPUTE_OFFSETS || (D == 128 && !CAUSAL && BN == 64);
   int koff_live[D / 16], voff_live[D / 32][2];
   frag_offsets(lane, koff_live, voff_live);
   auto fresh_offsets = [&](int (&ko)[D / 16], int (&vo)[D / 32][2]) __attribute__((always_inline)) {
-    if constexpr (RECOMPUTE_OFFSETS) {
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      frag_offsets(ln, ko, vo);
-    }
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    frag_offsets(ln, ko, vo);
   };
   // Direct-to-LDS loads: load i of a tile fills LDS bytes [1024 i, 1024 i + 1024),
   // i.e. rows ROWS_PER_DMA*i.. of the tile; lane l fills tile row
@@ -325,11 +326,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   int n_full = full_end > kb ? (full_end - kb) / BN : 0;
   if (n_full > ntiles) n_full = ntiles;
 
-  auto pv = [&](const short* vbuf) {
-    int ko_new[D / 16], vo_new[D / 32][2];
-    fresh_offsets(ko_new, vo_new);
-    const int(&koff)[D / 16] = RECOMPUTE_OFFSETS ? ko_new : koff_live;
-    const int(&voff)[D / 32][2] = RECOMPUTE_OFFSETS ? vo_new : voff_live;
+  auto pv = [&](const short* vbuf, const int (&voff)[D / 32][2]) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -343,6 +340,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
       }
     }
   };
+  // P V outside a tile step (a causal tile in this wave's future, the last tile)
+  auto pv_outside = [&](const short* vbuf) {
+    if constexpr (RECOMPUTE_MASKED) {
+      int ko_new[D / 16], vo_new[D / 32][2];
+      fresh_offsets(ko_new, vo_new);
+      pv(vbuf, vo_new);
+    } else {
+      pv(vbuf, voff_live);
+    }
+  };
 
   // One key tile: S = K(j) Q^T, then (if HAVE_PREV) the pending U += V(j-1)^T P(j-1)^T,
   // then the softmax of S into pprev.
@@ -351,10 +358,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     constexpr bool HAVE_PREV = decltype(prev_tag)::value;
     // ---- S^T = K_tile Q^T: each K fragment feeds QB MFMAs ----
     constexpr bool PRIO_ALL = kRaisePvPriority && D == 64;
+    constexpr bool FRESH = MASK ? RECOMPUTE_MASKED : RECOMPUTE_OFFSETS;
     int ko_new[D / 16], vo_new[D / 32][2];
-    fresh_offsets(ko_new, vo_new);
-    const int(&koff)[D / 16] = RECOMPUTE_OFFSETS ? ko_new : koff_live;
-    const int(&voff)[D / 32][2] = RECOMPUTE_OFFSETS ? vo_new : voff_live;
+    if constexpr (FRESH) fresh_offsets(ko_new, vo_new);
+    const int(&koff)[D / 16] = FRESH ? ko_new : koff_live;
+    const int(&voff)[D / 32][2] = FRESH ? vo_new : voff_live;
     f32x16 s[QB][BN / 32];
     if constexpr (PRIO_ALL) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
@@ -373,7 +381,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     // ---- the previous tile's P V: MFMA work that does not wait for this softmax ----
     if constexpr (HAVE_PREV) {
       if constexpr (kRaisePvPriority && !PRIO_ALL) __builtin_amdgcn_s_setprio(2);
-      pv(vprev);
+      pv(vprev, voff);
     }
     if constexpr (kRaisePvPriority) __builtin_amdgcn_s_setprio(0);
     // s[qb][kb][r]: raw score of query wq0 + 32 qb + l32, key n0 + 32 kb + 8(r/4) + 4 hi + r%4.
@@ -492,7 +500,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     if (j + 1 < ntiles) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
     issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
     if (CAUSAL && n0 > wq0 + 32 * QB - 1 + off) {   // whole tile in this wave's future
-      if (have_prev) pv(v_rd);
+      if (have_prev) pv_outside(v_rd);
       have_prev = false;
       continue;
     }
@@ -501,7 +509,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     have_prev = true;
   }
   sync_tile();                                  // V of the last tile is in LDS
-  if (have_prev) pv(((ntiles - 1) & 1) ? lds_v1 : lds_v0);
+  if (have_prev) pv_outside(((ntiles - 1) & 1) ? lds_v1 : lds_v0);
 
   // ---- epilogue: O = U / l, LSE = ln2 (ref + log2 l) ----
   write_rows<D, BF16, QB>(p, sl, bh, wi.split, wq0, lane, acc_o, ref, l_run);
