@@ -284,16 +284,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
       dp = mfma_32x32x16<BF16>(b, dof[ks], dp);
     }
     // s[r], dp[r]: key n0 + 8 (r / 4) + 4 hi + r % 4, query qrow
+    // The mask is applied to the whole tile behind one wave-uniform branch: a block
+    // this size is not speculated into per-score selects on the unmasked tiles.
+    float pr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+    if (mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = n0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (key >= Nk || (CAUSAL && key > qrow + off)) pr[r] = 0.f;
+      }
+    }
     float ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-      if (mask) {
-        const int key = n0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (key >= Nk || (CAUSAL && key > qrow + off)) pr = 0.f;
-      }
-      ds[r] = pr * (dp[r] - dl);
-    }
+    for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (dp[r] - dl);
     i16x8 dsp[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -473,31 +478,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       else vk = vf[ks];
       dp = mfma_32x32x16<BF16>(b, vk, dp);
     }
-    // s[r], dp[r]: query t BQ + 8 (r / 4) + 4 hi + r % 4, key `key`. Each half (8
-    // rows) is rounded and packed as soon as it is computed.
+    // s[r], dp[r]: query t BQ + 8 (r / 4) + 4 hi + r % 4, key `key`.
     i16x8 pp[2], dsp[2];
+    if constexpr (D == 64) {
+      // The mask is applied to the whole tile behind one wave-uniform branch (a block
+      // this size is not speculated into per-score selects on the unmasked tiles).
+      float w[16];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      float e1[8], e2[8];
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int g = 2 * tt + gg;
+      for (int g = 0; g < 4; ++g) {
         typedef float f32x4 __attribute__((ext_vector_type(4)));
         const f32x4 l4 = *(const f32x4*)(lsb + 8 * g + 4 * hi);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          float w = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l4[e]));
-          if (mask) {
-            const int query = t * BQ + 8 * g + 4 * hi + e;
-            if (query >= Nq || (CAUSAL && key_rel > query)) w = 0.f;
-          }
-          e1[4 * gg + e] = w;
-          e2[4 * gg + e] = w * dp[r];
+        for (int e = 0; e < 4; ++e) w[4 * g + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -l4[e]));
+      }
+      if (mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int query = t * BQ + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (query >= Nq || (CAUSAL && key_rel > query)) w[r] = 0.f;
         }
       }
-      pp[tt] = pack8<BF16>(e1);
-      dsp[tt] = pack8<BF16>(e2);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float e1[8], e2[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          e1[i] = w[8 * tt + i];
+          e2[i] = w[8 * tt + i] * dp[8 * tt + i];
+        }
+        pp[tt] = pack8<BF16>(e1);
+        dsp[tt] = pack8<BF16>(e2);
+      }
+    } else {
+      // At d = 128 the sixteen weights of the tile cannot all stay live (the kernel
+      // spills): each half (8 rows) is masked, rounded and packed as it is computed.
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float e1[8], e2[8];
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const int g = 2 * tt + gg;
+          typedef float f32x4 __attribute__((ext_vector_type(4)));
+          const f32x4 l4 = *(const f32x4*)(lsb + 8 * g + 4 * hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float wr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l4[e]));
+            if (mask) {
+              const int query = t * BQ + 8 * g + 4 * hi + e;
+              if (query >= Nq || (CAUSAL && key_rel > query)) wr = 0.f;
+            }
+            e1[4 * gg + e] = wr;
+            e2[4 * gg + e] = wr * dp[r];
+          }
+        }
+        pp[tt] = pack8<BF16>(e1);
+        dsp[tt] = pack8<BF16>(e2);
+      }
     }
     // dV^T += dO^T P, dK^T += Q^T dS
 #pragma unroll
