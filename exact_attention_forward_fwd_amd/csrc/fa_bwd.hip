@@ -98,8 +98,22 @@ __global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdParams p) {
 
 // Work item of a workgroup out of T: slice and block of 128 rows (queries for dQ,
 // keys for dK/dV). Contiguous ranges per XCD, so the blocks of one slice share an L2.
+//
+// Under a causal mask the blocks differ in length (dQ: the last query blocks see
+// the most keys; dK/dV: the first key blocks are seen by the most queries). Then all
+// slices' longest blocks go first, slice index fastest: with the slice count a
+// multiple of 8 each XCD (blockIdx mod 8) keeps a fixed eighth of the slices and
+// runs their blocks longest first. HEAVY_LAST: the longest block is the last one.
+template <bool CAUSAL, bool HEAVY_LAST>
 __device__ __forceinline__ void bwd_item(int T, int nblocks, int& bh, int& blk) {
   const int bid = blockIdx.x;
+  if (CAUSAL) {
+    const int slices = T / nblocks;
+    const int rank = bid / slices;
+    bh = bid - rank * slices;
+    blk = HEAVY_LAST ? nblocks - 1 - rank : rank;
+    return;
+  }
   const int xcd = bid & 7, slot = bid >> 3, per = T >> 3, rem = T & 7;
   const int w = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
   bh = w / nblocks;
@@ -213,7 +227,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   __shared__ __attribute__((aligned(1024))) short lds_v1[TILE];
 
   int bh, blk;
-  bwd_item(p.dq_wgs, p.qblocks, bh, blk);
+  bwd_item<CAUSAL, true>(p.dq_wgs, p.qblocks, bh, blk);
   if (CAUSAL) blk = p.qblocks - 1 - blk;   // longest rows first
   const int Nq = p.Nq, Nk = p.Nk, off = p.off;
   const int m0 = blk * BM;
@@ -372,7 +386,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(256))) float lds_d1[64];
 
   int bhk, blk;                                 // K/V slice (batch, K/V head) and key block
-  bwd_item(p.dkdv_wgs, p.kblocks, bhk, blk);
+  bwd_item<CAUSAL, false>(p.dkdv_wgs, p.kblocks, bhk, blk);
   const int Nq = p.Nq, Nk = p.Nk, off = p.off, group = p.group;
   const int hk_count = p.Hq / group;
   const int b = bhk / hk_count, kh = bhk - b * hk_count;

@@ -78,6 +78,18 @@ template <bool CAUSAL>
 __device__ __forceinline__ WorkItem work_item(const Params& p) {
   const int bid = blockIdx.x;
   const int T = p.total_wgs;
+  if (CAUSAL) {
+    // Causal row blocks differ in length (block mb sees mb + 1 blocks of keys): all
+    // slices' longest blocks first, slice index fastest. Workgroup b runs on XCD b mod
+    // 8, so with the slice count a multiple of 8 each XCD keeps a fixed eighth of the
+    // slices and runs their blocks longest first. Measured against slice-contiguous
+    // ranges per XCD: +17% (n2048 d128), +25% (n1000 d64), +26% (n4096 d64); +10% to
+    // +23% with 12 or 36 slices, where a slice's blocks spread over the XCDs.
+    const int slices = T / (p.num_m_blocks * p.num_splits);
+    const int rank = bid / slices, bh = bid - rank * slices;
+    const int mb_rank = rank / p.num_splits, split = rank - mb_rank * p.num_splits;
+    return {bh, split, p.num_m_blocks - 1 - mb_rank};
+  }
   const int xcd = bid & 7, slot = bid >> 3, per = T >> 3, rem = T & 7;
   const int w = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
   const int per_slice = p.num_m_blocks * p.num_splits;
