@@ -1066,12 +1066,15 @@ void default_tile(int64_t N, int64_t d, int causal, int* bm, int* bn) {
 }
 
 
-// Resident workgroups per CU: the four-wave tiles run two waves per SIMD (2 per CU),
-// the eight-wave tiles one workgroup per CU; the 2-wave (64, 64) tile fits two waves
-// per SIMD at d = 64 (4 per CU) but needs more than 256 registers at d = 128 (2 per CU).
-int wgs_per_cu(int bm, int64_t d) {
+// Resident workgroups per CU, from each tile's registers (a SIMD holds 512 per
+// lane): the four-wave tiles run one wave per SIMD per workgroup, two workgroups
+// per CU at 160..256 registers and three for the 32-key tiles at d = 64 (147..160);
+// the 2-wave (64, 64) tile fits two waves per SIMD at d = 64 (4 per CU) but needs
+// more than 256 registers at d = 128 (2 per CU); the eight-wave tiles fill a CU.
+int wgs_per_cu(int bm, int bn, int64_t d) {
   if (bm == 64) return d == 64 ? 4 : 2;
-  return bm == 128 ? 2 : 1;
+  if (bm == 128) return (d == 64 && bn == 32) ? 3 : 2;
+  return 1;
 }
 
 // Key ranges per query block for split-KV. Measured on MI355X: a split pays when the
@@ -1083,7 +1086,7 @@ int wgs_per_cu(int bm, int64_t d) {
 int split_heuristic(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d, int bm, int bn) {
   if (B <= 0 || Hq <= 0 || Nq <= 0 || Nk <= 0) return 1;
   const int64_t base = B * Hq * ((Nq + bm - 1) / bm);
-  const int64_t slots = 256 * (int64_t)(2 * Nq <= bm ? 1 : wgs_per_cu(bm, d));
+  const int64_t slots = 256 * (int64_t)(2 * Nq <= bm ? 1 : wgs_per_cu(bm, bn, d));
   if (base >= slots) return 1;
   const int64_t tiles = (Nk + bn - 1) / bn;
   int64_t sp = slots / base;
