@@ -57,11 +57,14 @@ __device__ __forceinline__ i16x8 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 }
 // 16 bytes per lane straight from memory into LDS: lane l writes LDS bytes
 // [lds + 16 l, lds + 16 l + 16) (lds is wave-uniform); out-of-range lanes write zeros.
+// AUX: the cache-policy bits of the load (0: default; 2: non-temporal, for data read
+// once).
+template <int AUX = 0>
 __device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, short* lds, uint32_t voff,
                                                      uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       r, (__attribute__((address_space(3))) void*)((__attribute__((address_space(3))) short*)lds), 16, voff, soff,
-      0, 0);
+      0, AUX);
 }
 
 // K and V tiles sit in LDS without padding, as rows of D 16-bit elements whose

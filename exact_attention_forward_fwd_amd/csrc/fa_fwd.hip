@@ -294,12 +294,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     dma_off_k[kk] = (uint32_t)((r_local * p.k_sr + col) * 2);
     dma_off_v[kk] = (uint32_t)((r_local * p.v_sr + col) * 2);
   }
+  // The 2-wave tile serves decoding (one to a few query rows per K/V head) and short
+  // sequences, where every K/V byte is read about once: its loads are non-temporal
+  // at d = 128 (measured on long-context decoding: 5.4 -> 5.7 TB/s at 32 key ranges,
+  // 5.6 -> 6.4 at 64; neutral at d = 64, and 9-11% slower on the causal four-wave tiles,
+  // whose K/V tiles are re-read from L2 by every row block).
+  constexpr int LOAD_AUX = (NW == 2 && D == 128) ? 2 : 0;
   auto issue_tile_load = [&](const __amdgpu_buffer_rsrc_t& rsrc, const uint32_t (&lane_off)[DMA_PER_WAVE], int sr,
                              short* dst, int n0) {
 #pragma unroll
     for (int kk = 0; kk < DMA_PER_WAVE; ++kk) {
       const int i = kk * NW + wave;
-      buffer_load16_to_lds(rsrc, dst + 512 * i, lane_off[kk], (uint32_t)((n0 + ROWS_PER_DMA * i) * sr * 2));
+      buffer_load16_to_lds<LOAD_AUX>(rsrc, dst + 512 * i, lane_off[kk], (uint32_t)((n0 + ROWS_PER_DMA * i) * sr * 2));
     }
   };
 
@@ -1082,11 +1088,13 @@ int wgs_per_cu(int bm, int bn, int64_t d) {
 // filled once (a second round of workgroups costs more than the shorter ranges save)
 // with ranges of at least 8 key tiles, below which the per-workgroup prologue and
 // the merge dominate. Decoding-like shapes (a single, mostly empty query block per
-// slice) stream K and V at the memory's pace and do best with one workgroup per CU.
+// slice) stream K and V at the memory's pace and do best with two workgroups per CU
+// (measured with non-temporal loads: 6.4 against 5.7 TB/s with one per CU at d = 128,
+// 5.6 against 5.0 at d = 64, 32 query heads over 8 K/V heads, 128K keys).
 int split_heuristic(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d, int bm, int bn) {
   if (B <= 0 || Hq <= 0 || Nq <= 0 || Nk <= 0) return 1;
   const int64_t base = B * Hq * ((Nq + bm - 1) / bm);
-  const int64_t slots = 256 * (int64_t)(2 * Nq <= bm ? 1 : wgs_per_cu(bm, bn, d));
+  const int64_t slots = 256 * (int64_t)(2 * Nq <= bm ? 2 : wgs_per_cu(bm, bn, d));
   if (base >= slots) return 1;
   const int64_t tiles = (Nk + bn - 1) / bn;
   int64_t sp = slots / base;
