@@ -525,7 +525,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     } else {
       // At d = 128 the sixteen weights of the tile cannot all stay live (the kernel
-      // spills): each half (8 rows) is masked, rounded and packed as it is computed.
+      // spills): each half (8 rows) is formed, masked behind one wave-uniform branch,
+      // rounded and packed in turn.
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         float e1[8], e2[8];
@@ -535,17 +536,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           typedef float f32x4 __attribute__((ext_vector_type(4)));
           const f32x4 l4 = *(const f32x4*)(lsb + 8 * g + 4 * hi);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float wr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -l4[e]));
-            if (mask) {
-              const int query = t * BQ + 8 * g + 4 * hi + e;
-              if (query >= Nq || (CAUSAL && key_rel > query)) wr = 0.f;
-            }
-            e1[4 * gg + e] = wr;
-            e2[4 * gg + e] = wr * dp[r];
+          for (int e = 0; e < 4; ++e) e1[4 * gg + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -l4[e]));
+        }
+        if (mask) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int query = t * BQ + 8 * (2 * tt + (i >> 2)) + 4 * hi + (i & 3);
+            if (query >= Nq || (CAUSAL && key_rel > query)) e1[i] = 0.f;
           }
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e2[i] = e1[i] * dp[8 * tt + i];
         pp[tt] = pack8<BF16>(e1);
         dsp[tt] = pack8<BF16>(e2);
       }
