@@ -917,21 +917,26 @@ struct MergeParams {
   int64_t o_sb, o_sh;
 };
 
-template <int D, bool BF16>
+template <int D, bool BF16, int G>
 __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
 #pragma clang fp contract(off)
-  constexpr int LPR = D / 2;                 // lanes per row
-  constexpr int RPB = 256 / LPR;             // rows per workgroup
+  constexpr int LPR = D / 4;                 // lanes per row and group (4 columns each)
+  constexpr int RPB = 256 / (LPR * G);       // rows per workgroup
   using f32x2 = float __attribute__((ext_vector_type(2)));
+  using f32x4 = float __attribute__((ext_vector_type(4)));
   using e16x2 = typename std::conditional<BF16, __bf16 __attribute__((ext_vector_type(2))),
                                           _Float16 __attribute__((ext_vector_type(2)))>::type;
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ float wts[RPB][kMaxSplits];
-  const int rl = (int)threadIdx.x / LPR;     // row within the workgroup
-  const int j = (int)threadIdx.x % LPR;      // lane within the row
+  __shared__ f32x4 part[G > 1 ? RPB : 1][G][LPR];
+  const int tid = (int)threadIdx.x;
+  const int j = tid % LPR;                   // lane within the row's group
+  const int grp = (tid / LPR) % G;           // group: ranges grp, grp + G, ...
+  const int rl = tid / (LPR * G);            // row within the workgroup
   const int row = blockIdx.x * RPB + rl;
   const bool live = row < m.rows;
   const int64_t stride = m.rows;             // between the partials of consecutive ranges
+  // every group forms the same weights; group 0 stores them
   float mx = -INFINITY;
   if (live)
     for (int k = j; k < m.splits; k += LPR) mx = fmaxf(mx, m.plse[k * stride + row]);
@@ -941,35 +946,47 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
   if (live && mx != -INFINITY)
     for (int k = j; k < m.splits; k += LPR) {
       const float e = __builtin_amdgcn_exp2f((m.plse[k * stride + row] - mx) * kLog2e);
-      wts[rl][k] = e;
+      if (grp == 0) wts[rl][k] = e;
       sum += e;
     }
 #pragma unroll
   for (int w = LPR / 2; w > 0; w >>= 1) sum += __shfl_xor(sum, w, LPR);
   __syncthreads();
-  if (!live) return;
-  f32x2 acc = {0.f, 0.f};
-  float lse = -INFINITY;
-  if (mx != -INFINITY) {                     // sum >= 1: the maximal range contributes 1
-    const float* src = m.po + (int64_t)row * D + 2 * j;
-    const int64_t step = stride * D;
-    int k = 0;
-    for (; k + 8 <= m.splits; k += 8) {
-      f32x2 x[8];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (live && mx != -INFINITY) {             // sum >= 1: the maximal range contributes 1
+    // the partials are read once: 16-byte non-temporal loads
+    const f32x4* src = (const f32x4*)(m.po + (int64_t)row * D + 4 * j);
+    const int64_t step = stride * D / 4;
+    int k = grp;
+    for (; k + 7 * G < m.splits; k += 8 * G) {
+      f32x4 x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = *(const f32x2*)(src + (k + u) * step);
+      for (int u = 0; u < 8; ++u) x[u] = __builtin_nontemporal_load(src + (k + u * G) * step);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc += wts[rl][k + u] * x[u];
+      for (int u = 0; u < 8; ++u) acc += wts[rl][k + u * G] * x[u];
     }
-    for (; k < m.splits; ++k) acc += wts[rl][k] * *(const f32x2*)(src + k * step);
-    const float inv = 1.f / sum;
-    acc *= inv;
+    for (; k < m.splits; k += G) acc += wts[rl][k] * __builtin_nontemporal_load(src + k * step);
+  }
+  if constexpr (G > 1) {
+    part[rl][grp][j] = acc;
+    __syncthreads();
+    if (grp != 0) return;
+#pragma unroll
+    for (int g = 1; g < G; ++g) acc += part[rl][g][j];
+  }
+  if (!live) return;
+  float lse = -INFINITY;
+  if (mx != -INFINITY) {
+    acc *= 1.f / sum;
     lse = mx + kLn2 * __builtin_amdgcn_logf(sum);
   }
   const int bh = row / m.Nq, i = row - bh * m.Nq;
   const int b = bh / m.Hq, h = bh - b * m.Hq;
-  short* orow = m.o + b * m.o_sb + h * m.o_sh + (int64_t)i * m.o_sr + 2 * j;
-  *(uint32_t*)orow = __builtin_bit_cast(uint32_t, __builtin_convertvector(acc, e16x2));
+  short* orow = m.o + b * m.o_sb + h * m.o_sh + (int64_t)i * m.o_sr + 4 * j;
+  const e16x2 lo = __builtin_convertvector((f32x2){acc[0], acc[1]}, e16x2);
+  const e16x2 hi2 = __builtin_convertvector((f32x2){acc[2], acc[3]}, e16x2);
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  *(u32x2*)orow = (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi2)};
   if (j == 0) m.lse[row] = lse;
 }
 
@@ -988,8 +1005,13 @@ constexpr TileShape kTiles[] = {
 
 template <int D, bool BF16>
 hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
-  constexpr int RPB = 256 / (D / 2);
-  hipLaunchKernelGGL((fa_merge_kernel<D, BF16>), dim3((m.rows + RPB - 1) / RPB), dim3(256), 0, stream, m);
+  // Few rows (decoding): eight lane groups per row share its ranges, so that the
+  // grid has enough workgroups and each lane fewer dependent load rounds.
+  constexpr int RPB1 = 256 / (D / 4), RPB8 = RPB1 / 8;
+  if ((m.rows + RPB1 - 1) / RPB1 < 512)
+    hipLaunchKernelGGL((fa_merge_kernel<D, BF16, 8>), dim3((m.rows + RPB8 - 1) / RPB8), dim3(256), 0, stream, m);
+  else
+    hipLaunchKernelGGL((fa_merge_kernel<D, BF16, 1>), dim3((m.rows + RPB1 - 1) / RPB1), dim3(256), 0, stream, m);
   return hipGetLastError();
 }
 
