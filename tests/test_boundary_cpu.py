@@ -91,6 +91,16 @@ def test_general_entry_validation_without_gpu():
     assert call_ex(q=None, k=None, v=None, o=None, lse=None, Hq=0, Hk=0) == 0
 
 
+def test_key_count_limit_without_gpu():
+    """One key beyond the 32-bit slice range ((N + 512) * row stride < 2^30 elements) is
+    refused before any launch; the GPU tests run the largest accepted count."""
+    for d in (64, 128):
+        nk = (1 << 30) // d - 513 + 1
+        assert call_ex(Hq=4, Hk=1, Nq=1, Nk=nk, d=d) == 7
+        assert call_ex(Hq=4, Hk=1, Nq=1, Nk=nk - 1, d=d, ks=(0, 0, 2 * d)) == 7   # a wider row stride counts
+        assert call_split(Hq=4, Hk=1, Nq=1, Nk=nk, d=d, ws=A, ws_bytes=1 << 20) == 7
+
+
 def call_split(ws=None, ws_bytes=0, splits=2, q=A, B=1, Hq=4, Hk=2, Nq=64, Nk=100, d=64, causal=0, bm=0, bn=0):
     return fa.fa_fwd_split(q, A, A, A, A, B, Hq, Hk, Nq, Nk, d, None, None, None, None, 0.125, causal, 0, None,
                            bm, bn, splits, ws, ws_bytes)

@@ -1,0 +1,110 @@
+"""GPU checks at the largest key count the library accepts (the 32-bit byte range of
+one K/V slice: (N + 512) * row stride < 2^30 elements), through the C ABI.
+
+At this size the oracle's own pass over 8-17 million keys per row would dominate, so
+the inputs are built so that the exact result has a closed form that holds at any
+size (the definition of attention, evaluated by hand):
+
+- Q = 0: every visible key gets the same weight, so O is the mean of V over the keys
+  and LSE = ln N_k. V[j, c] = ((j + c) mod 7 - 3) / 4 is exact in both 16-bit types,
+  so the mean is a sum of residue counts. Every key of the range must be read once.
+- K = 0 except the last key, which aligns with q: that key's score z = 40 dominates
+  every other weight (e^-40 N_k < 1e-10), so O = V[last] and
+  LSE = z + ln(1 + (N_k - 1) e^-z). The last key sits at the top of the addressable
+  range.
+
+Both the unsplit general entry point (packed decoding: one query row for each of 4
+query heads over one K/V head) and split-KV at the suggested count are checked; both
+must accept this N_k (the binding raises on any other status). That N_k + 1 is
+refused is checked without a GPU, in the boundary tests.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_forward_fwd_amd as fa
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+TOL_O = {"f16": 2e-3, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.load_library()
+    yield
+
+
+def _max_keys(d):
+    return (1 << 30) // d - 512 - 1
+
+
+def _pattern_v(nk, d, dtype):
+    table = torch.tensor([[((r + c) % 7 - 3) / 4 for c in range(d)] for r in range(7)], dtype=torch.float32)
+    idx = torch.arange(nk, device=DEV) % 7
+    return table.to(DEV).to(TORCH_DT[dtype])[idx].reshape(1, 1, nk, d)
+
+
+def _pattern_mean(nk, d):
+    """Mean over j < nk of ((j + c) mod 7 - 3) / 4, per column c, from residue counts."""
+    out = np.zeros(d)
+    for c in range(d):
+        tot = 0.0
+        for r in range(7):
+            cnt = nk // 7 + (1 if (r - c) % 7 < nk % 7 else 0)   # j = r - c (mod 7)
+            tot += cnt * (r - 3) / 4
+        out[c] = tot / nk
+    return out
+
+
+def _run(q, k, v, splits, scale):
+    if splits is None:
+        return fa.fwd_ex(q, k, v, scale=scale, causal=False)
+    return fa.fwd_split(q, k, v, scale=scale, causal=False, num_splits=splits)
+
+
+@pytest.mark.parametrize("d,dtype", [(128, "bf16"), (64, "f16")])
+def test_largest_key_count(d, dtype):
+    nk = _max_keys(d)
+    scale = 1 / math.sqrt(d)
+    hq = 4
+    print(f"[limits] d={d} {dtype} Nk={nk}", flush=True)
+    k = torch.zeros((1, 1, nk, d), dtype=TORCH_DT[dtype], device=DEV)
+    v = _pattern_v(nk, d, dtype)
+    suggested = fa.fa_split_default(1, hq, 1, 1, nk, d, False)
+    assert suggested > 1
+
+    # Q = 0: uniform weights
+    q = torch.zeros((1, hq, 1, d), dtype=TORCH_DT[dtype], device=DEV)
+    mean = _pattern_mean(nk, d)
+    for splits in (None, suggested):
+        o, lse = _run(q, k, v, splits, scale)
+        torch.cuda.synchronize()
+        err_o = np.abs(o.float().cpu().double().numpy()[0, :, 0] - mean[None, :]).max()
+        err_l = np.abs(lse.cpu().double().numpy() - math.log(nk)).max()
+        print(f"[limits]   Q=0 splits={splits}: max|dO| {err_o:.2e} max|dLSE| {err_l:.2e}", flush=True)
+        assert err_o <= TOL_O[dtype] and err_l <= 1e-3
+
+    # one dominant key at the top of the range
+    t = 40.0 / scale                             # stored rounded to the dtype; z is taken from that value
+    k[0, 0, nk - 1, 0] = t
+    t16 = float(k[0, 0, nk - 1, 0].float())
+    q[..., 0] = 1.0
+    z = scale * t16
+    lse_ref = z + math.log1p((nk - 1) * math.exp(-z))
+    v_last = v[0, 0, nk - 1].float().cpu().double().numpy()
+    for splits in (None, suggested):
+        o, lse = _run(q, k, v, splits, scale)
+        torch.cuda.synchronize()
+        err_o = np.abs(o.float().cpu().double().numpy()[0, :, 0] - v_last[None, :]).max()
+        err_l = np.abs(lse.cpu().double().numpy() - lse_ref).max()
+        print(f"[limits]   last key splits={splits}: max|dO| {err_o:.2e} max|dLSE| {err_l:.2e}", flush=True)
+        assert err_o <= TOL_O[dtype] and err_l <= 1e-3
+    del k, v
+    torch.cuda.empty_cache()
+
