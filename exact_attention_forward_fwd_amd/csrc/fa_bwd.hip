@@ -304,11 +304,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 #pragma unroll
     for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
     if (mask) {
+      // hidden: key >= Nk or (causal) key > qrow + off, i.e. key > min(Nk - 1, qrow + off);
+      // one compare per score against the lane's limit
+      const int lim = (CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1) - (n0 + 4 * hi);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = n0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (key >= Nk || (CAUSAL && key > qrow + off)) pr[r] = 0.f;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > lim) pr[r] = 0.f;
     }
     float ds[16];
 #pragma unroll
@@ -341,7 +342,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     }
     const int n0 = j * BN;
     if (CAUSAL && n0 > wq0 + 31 + off) return;   // whole tile in this wave's future
-    const bool mask = j >= n_full;
+    // a tile needs the mask if it reaches past Nk or, under a causal mask, past the
+    // diagonal of this wave's first query (decided per wave, not per workgroup)
+    const bool mask = n0 + BN > Nk || (CAUSAL && n0 + BN - 1 > wq0 + off);
     if constexpr (D == 64 && !CAUSAL) {
       if (mask) step(n0, k_rd, v_rd, std::true_type{});
       else step(n0, k_rd, v_rd, std::false_type{});
@@ -457,6 +460,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
   };
 
+  // Score r of query tile t belongs to query t BQ + 4 hi + q_r, q_r = 8 (r / 4) + r % 4.
+  // It is hidden when the query is past Nq or (causal) before this lane's key_rel:
+  // two compares of q_r against the lane's limits.
+  struct MaskLimits {
+    int last, first;   // visible iff first <= q_r <= last
+    __device__ bool hidden(int q_r) const { return q_r > last || (CAUSAL && q_r < first); }
+  };
+  auto mask_limits = [&](int t) __attribute__((always_inline)) {
+    const int q0 = t * BQ + 4 * hi;
+    return MaskLimits{Nq - 1 - q0, key_rel - q0};
+  };
   // `mask` as in the dQ kernel: a bool, or a compile-time constant at d = 64 without
   // a causal mask
   auto step = [&](int t, const short* qbuf, const short* obuf, const float* lsb, const float* db_, auto mask_arg)
@@ -506,11 +520,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int e = 0; e < 4; ++e) w[4 * g + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -l4[e]));
       }
       if (mask) {
+        const MaskLimits ml = mask_limits(t);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int query = t * BQ + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (query >= Nq || (CAUSAL && key_rel > query)) w[r] = 0.f;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (ml.hidden(8 * (r >> 2) + (r & 3))) w[r] = 0.f;
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -539,11 +552,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int e = 0; e < 4; ++e) e1[4 * gg + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -l4[e]));
         }
         if (mask) {
+          const MaskLimits ml = mask_limits(t);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int query = t * BQ + 8 * (2 * tt + (i >> 2)) + 4 * hi + (i & 3);
-            if (query >= Nq || (CAUSAL && key_rel > query)) e1[i] = 0.f;
-          }
+          for (int i = 0; i < 8; ++i)
+            if (ml.hidden(8 * (2 * tt + (i >> 2)) + (i & 3))) e1[i] = 0.f;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) e2[i] = e1[i] * dp[8 * tt + i];
