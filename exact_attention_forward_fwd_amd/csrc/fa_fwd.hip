@@ -335,12 +335,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   i16x8 pprev[QB][BN / 16];   // P of the previous tile as 16-bit B operands
 
   // Tile j holds keys kb + j BN ... Tiles [0, n_full) need no mask for any query of
-  // this workgroup; the rest (the causal diagonal band and the ragged last tile) do.
+  // this wave; the rest (the causal diagonal band and the ragged last tile) do.
   // Under a causal mask the workgroup's last query sees keys up to m0 + BM - 1 + off;
-  // none may be visible.
+  // none may be visible. Every wave passes through all ntiles tiles (one barrier
+  // each), the later waves of a causal workgroup with more of them unmasked.
   const int n_end = CAUSAL ? min(ke, m0 + BM + off) : ke;
   const int ntiles = n_end > kb ? (n_end - kb + BN - 1) / BN : 0;
-  const int full_end = CAUSAL ? min(ke, m0 + 1 + off) : ke;   // keys below it: valid for every query
+  const int full_end = CAUSAL ? min(ke, wq0 + 1 + off) : ke;   // keys below it: valid for every query of the wave
   int n_full = full_end > kb ? (full_end - kb) / BN : 0;
   if (n_full > ntiles) n_full = ntiles;
 
@@ -526,14 +527,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
       have_prev = false;
       continue;
     }
-    // Under a causal mask the workgroup's diagonal band is fully visible to the
-    // later waves up to their own diagonal: those tiles take the unmasked step
-    // (measured +1-1.6% on causal shapes). Not at d = 128 with 32-key tiles, where
-    // the extra copy of the step made the loop spill (-20%).
-    constexpr bool WAVE_FULL_STEP = CAUSAL && !(D == 128 && BN == 32);
-    const bool wave_full = WAVE_FULL_STEP && n0 + BN <= Nk && n0 + BN - 1 <= wq0 + off;
-    if (wave_full && have_prev) step(n0, k_rd, v_rd, std::false_type{}, std::true_type{});
-    else if (have_prev) step(n0, k_rd, v_rd, std::true_type{}, std::true_type{});
+    if (have_prev) step(n0, k_rd, v_rd, std::true_type{}, std::true_type{});
     else step(n0, k_rd, v_rd, std::true_type{}, std::false_type{});
     have_prev = true;
   }
