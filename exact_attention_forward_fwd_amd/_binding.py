@@ -165,6 +165,31 @@ def _dtype_code(t):
     raise TypeError(f"dtype must be float16 or bfloat16, got {t.dtype}")
 
 
+def _check_tensor(name, t, device, shape=None, dtype=None, contiguous=False, last_contiguous=False):
+    """Raise ValueError unless ``t`` is a GPU tensor on ``device`` with the given shape,
+    dtype and layout. Every pointer handed to the library passes through here: a host
+    pointer or an undersized buffer would reach a kernel as a bad address."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a GPU tensor on {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if last_contiguous and t.dim() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name}'s last dimension must be contiguous")
+
+
+def _workspace_args(workspace, device):
+    """(pointer, bytes) of a caller's workspace tensor (contiguous, on the GPU), or (0, 0)."""
+    if workspace is None:
+        return 0, 0
+    _check_tensor("workspace", workspace, device, contiguous=True)
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def fwd(q, k, v, scale: float | None = None, causal: bool = False, block_m: int | None = None,
         block_n: int | None = None, out=None, lse=None, stream=None):
     """Attention forward on torch tensors [B, H, N, d] (contiguous, same device/dtype).
@@ -186,12 +211,16 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, block_m: int 
         raise ValueError("q, k, v must share a dtype")
     B, H, N, d = q.shape
     dt = _dtype_code(q)
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _check_tensor("out", out, q.device, shape=q.shape, dtype=q.dtype, contiguous=True)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check_tensor("lse", lse, q.device, shape=(B, H, N), dtype=torch.float32, contiguous=True)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -221,16 +250,16 @@ def _general_args(q, k, v, scale, out, lse, stream):
     B, Hq, Nq, d = q.shape
     if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
         raise ValueError("k and v must be [B, Hk, Nk, d] with q's B and d")
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    if out.shape != q.shape or out.stride(-1) != 1:
-        raise ValueError("out must be shaped like q with a contiguous last dimension")
+    _check_tensor("out", out, q.device, shape=q.shape, dtype=q.dtype, last_contiguous=True)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
-    if not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Nq):
-        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    _check_tensor("lse", lse, q.device, shape=(B, Hq, Nq), dtype=torch.float32, contiguous=True)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -274,8 +303,7 @@ def fwd_split(q, k, v, scale: float | None = None, causal: bool = False, num_spl
     need = fa_split_workspace_bytes(B, Hq, Nq, d, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else 0
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace_args(workspace, q.device)
     st = fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hk,
                       Nq, Nk, d, q.stride()[:3], k.stride()[:3], v.stride()[:3], out.stride()[:3],
                       float(scale), causal, _dtype_code(q), sp, bm, bn, num_splits, ws_ptr, ws_bytes)
@@ -298,22 +326,26 @@ def bwd(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = False,
         if t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError(f"{name} must match q's shape and dtype")
     B, H, N, d = q.shape
-    if not lse.is_contiguous() or tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(name, t, q.device)
+    _check_tensor("lse", lse, q.device, shape=(B, H, N), dtype=torch.float32, contiguous=True)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, q.device, shape=q.shape, dtype=q.dtype, contiguous=True)
     need = fa_bwd_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = _workspace_args(workspace, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                 dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), causal, _dtype_code(q),
-                workspace.data_ptr(), workspace.numel() * workspace.element_size(), sp)
+                ws_ptr, ws_bytes, sp)
     if st != 0:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
@@ -334,21 +366,26 @@ def bwd_ex(q, k, v, o, dout, lse, scale: float | None = None, causal: bool = Fal
     if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
         raise ValueError("k and v must be [B, Hk, Nk, d] with q's B and d")
     Hk, Nk = k.shape[1], k.shape[2]
-    if not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32:
-        raise ValueError("lse must be a contiguous float32 [B, Hq, Nq] tensor")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(name, t, q.device)
+    _check_tensor("lse", lse, q.device, shape=(B, Hq, Nq), dtype=torch.float32, contiguous=True)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_tensor("dq", dq, q.device, shape=q.shape, dtype=q.dtype, contiguous=True)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, q.device, shape=k.shape, dtype=q.dtype, contiguous=True)
     if workspace is None:
         workspace = torch.empty(max(fa_bwd_workspace_bytes(B, Hq, Nq), 16), dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = _workspace_args(workspace, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     sp = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     st = fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hk, Nq, Nk, d, float(scale), causal,
-                   _dtype_code(q), workspace.data_ptr(), workspace.numel() * workspace.element_size(), sp)
+                   _dtype_code(q), ws_ptr, ws_bytes, sp)
     if st != 0:
         raise FaError(st, "fa_bwd_ex")
     return dq, dk, dv
