@@ -54,6 +54,8 @@ struct Params {
   int Hq;             // query heads
   int group;          // query heads per K/V head
   int causal_off;     // causal: key j is valid for query i iff j <= i + causal_off
+  int qmod;           // 0: row r of a slice is query r; > 0: the query heads of a group
+                      // are packed into one slice and row r is query r mod qmod
   int q_sr, k_sr, v_sr, o_sr;                      // row strides
   int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;   // batch and head strides
   uint32_t q_bytes, k_bytes, v_bytes;              // extent of one slice: rows past it read as zeros
@@ -339,9 +341,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   // Under a causal mask the workgroup's last query sees keys up to m0 + BM - 1 + off;
   // none may be visible. Every wave passes through all ntiles tiles (one barrier
   // each), the later waves of a causal workgroup with more of them unmasked.
-  const int n_end = CAUSAL ? min(ke, m0 + BM + off) : ke;
+  // Query indices of the workgroup's and the wave's rows: the rows themselves, or,
+  // with query heads packed (qmod > 0), any of 0 .. qmod - 1.
+  const bool packed = p.qmod > 0;
+  const int wg_last_q = packed ? p.qmod - 1 : m0 + BM - 1;
+  const int w_first_q = packed ? 0 : wq0;
+  const int w_last_q = packed ? p.qmod - 1 : wq0 + 32 * QB - 1;
+  const int n_end = CAUSAL ? min(ke, wg_last_q + 1 + off) : ke;
   const int ntiles = n_end > kb ? (n_end - kb + BN - 1) / BN : 0;
-  const int full_end = CAUSAL ? min(ke, wq0 + 1 + off) : ke;   // keys below it: valid for every query of the wave
+  const int full_end = CAUSAL ? min(ke, w_first_q + 1 + off) : ke;   // keys below it: valid for every query of the wave
   int n_full = full_end > kb ? (full_end - kb) / BN : 0;
   if (n_full > ntiles) n_full = ntiles;
 
@@ -410,7 +418,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     if constexpr (MASK) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int query = wq0 + 32 * qb + l32;
+        int query = wq0 + 32 * qb + l32;
+        if (CAUSAL && packed) query %= p.qmod;
         const int lim = (CAUSAL ? min(Nk - 1, query + off) : Nk - 1) - (n0 + 4 * hi);
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
@@ -522,7 +531,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     sync_tile();
     if (j + 1 < ntiles) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
     issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
-    if (CAUSAL && n0 > wq0 + 32 * QB - 1 + off) {   // whole tile in this wave's future
+    if (CAUSAL && n0 > w_last_q + off) {   // whole tile in this wave's future
       if (have_prev) pv_outside(v_rd);
       have_prev = false;
       continue;
@@ -619,13 +628,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // tiles the workgroup streams, tiles this wave computes, tiles it needs no mask
   // for; tile j holds keys kb + j BN ...
-  const int n_end = CAUSAL ? min(ke, m0 + BM + off) : ke;
+  // query indices of the rows, as in fa_fwd_kernel (packed query heads: any of 0 .. qmod - 1)
+  const bool packed = p.qmod > 0;
+  const int wg_last_q = packed ? p.qmod - 1 : m0 + BM - 1;
+  const int w_first_q = packed ? 0 : wq0;
+  const int w_last_q = packed ? p.qmod - 1 : wq0 + 32 * QB - 1;
+  const int n_end = CAUSAL ? min(ke, wg_last_q + 1 + off) : ke;
   const int T = n_end > kb ? (n_end - kb + BN - 1) / BN : 0;
   int Tw = 0, n_full = 0;
   if (wq0 < Nq) {
-    const int w_end = CAUSAL ? min(ke, wq0 + 32 * QB + off) : ke;
+    const int w_end = CAUSAL ? min(ke, w_last_q + 1 + off) : ke;
     Tw = w_end > kb ? (w_end - kb + BN - 1) / BN : 0;
-    const int full_end = CAUSAL ? min(ke, wq0 + 1 + off) : ke;
+    const int full_end = CAUSAL ? min(ke, w_first_q + 1 + off) : ke;
     n_full = min(Tw, full_end > kb ? (full_end - kb) / BN : 0);
   }
 
@@ -782,7 +796,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (mask) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const int query = wq0 + 32 * qb + l32;
+        int query = wq0 + 32 * qb + l32;
+        if (CAUSAL && packed) query %= p.qmod;
         // hidden: key > min(Nk - 1, query + off), as in the four-wave kernel
         const int lim = (CAUSAL ? min(Nk - 1, query + off) : Nk - 1) - (n0 + 4 * hi);
 #pragma unroll
@@ -1118,6 +1133,11 @@ int wgs_per_cu(int bm, int bn, int64_t d) {
 // slice) stream K and V at the memory's pace and do best with two workgroups per CU
 // (measured with non-temporal loads: 6.4 against 5.7 TB/s with one per CU at d = 128,
 // 5.6 against 5.0 at d = 64, 32 query heads over 8 K/V heads, 128K keys).
+// Grouped query heads with fewer rows than this per head are packed into one slice
+// per K/V head (decoding, a few draft tokens): one K/V stream serves the whole group.
+constexpr int64_t kPackRows = 64;
+bool packs_heads(int64_t Nq) { return Nq >= 1 && Nq < kPackRows; }
+
 int split_heuristic(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d, int bm, int bn) {
   if (B <= 0 || Hq <= 0 || Nq <= 0 || Nk <= 0) return 1;
   const int64_t base = B * Hq * ((Nq + bm - 1) / bm);
@@ -1158,19 +1178,28 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
   if ((st = read_strides(vs_in, Hk, Nk, d, vs)) != FA_OK) return st;
   if ((st = read_strides(os_in, Hq, Nq, d, os)) != FA_OK) return st;
   int64_t group = Hq / Hk;
-  // Decoding with grouped K/V heads: a single query row per head, so the query heads
-  // that share a K/V head become the rows of one slice (their rows are one head
-  // stride apart, and the lse rows [B, Hq, 1] are [B, Hk, group]). With one query
-  // row the bottom-right causal mask hides no key.
-  if (Nq == 1 && group > 1) {
-    qs[2] = qs[1];          // row r of the packed slice: query head r of the group
-    os[2] = os[1];
+  // Decoding with grouped K/V heads (fewer than kPackRows query rows per head): the
+  // query heads that share a K/V head become the rows of one slice, so that one
+  // workgroup streams each K/V tile once for all of them. With one row per head the
+  // rows are one head stride apart (and the bottom-right causal mask hides no key);
+  // with Nq rows per head q and o must be head-contiguous (head stride = Nq row
+  // strides), so that row g Nq + i of the slice is query i of head g, and the kernel
+  // takes the query index for the causal mask as row mod Nq. The lse rows
+  // [B, Hq, Nq] are [B, Hk, group Nq] either way.
+  int64_t qmod = 0;
+  if (group > 1 && packs_heads(Nq) && (Nq == 1 || (qs[1] == Nq * qs[2] && os[1] == Nq * os[2]))) {
+    if (Nq == 1) {
+      qs[2] = qs[1];        // row r of the packed slice: query head r of the group
+      os[2] = os[1];
+      causal = 0;
+    } else {
+      qmod = Nq;
+    }
     qs[1] *= group;         // next slice: the next group of query heads
     os[1] *= group;
-    Nq = group;
+    Nq *= group;
     Hq = Hk;
     group = 1;
-    causal = 0;
   }
   if (auto_tile) default_tile(Nq, d, causal, &bm, &bn);
   if (!rows_fit(Nq, qs[2]) || !rows_fit(Nq, os[2]) || !rows_fit(Nk, ks[2]) || !rows_fit(Nk, vs[2]))
@@ -1206,7 +1235,8 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
   p.Nk = (int)Nk;
   p.Hq = (int)Hq;
   p.group = (int)group;
-  p.causal_off = (int)(Nk - Nq);   // bottom-right alignment; 0 (top-left) when Nq = Nk
+  p.causal_off = (int)(Nk - (qmod > 0 ? qmod : Nq));   // bottom-right alignment; 0 (top-left) when Nq = Nk
+  p.qmod = (int)qmod;
   p.q_sb = qs[0]; p.q_sh = qs[1]; p.q_sr = (int)qs[2];
   p.k_sb = ks[0]; p.k_sh = ks[1]; p.k_sr = (int)ks[2];
   p.v_sb = vs[0]; p.v_sh = vs[1]; p.v_sr = (int)vs[2];
@@ -1292,10 +1322,10 @@ size_t fa_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d, in
 int fa_split_default(int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, int causal,
                      int block_m, int block_n) {
   if (B <= 0 || Hq <= 0 || Hk <= 0 || Hq % Hk || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 1;
-  if (Nq == 1 && Hq > Hk) {   // decoding with grouped heads: the group forms one slice
-    Nq = Hq / Hk;
+  if (Hq > Hk && packs_heads(Nq)) {   // grouped heads with few rows: the group forms one slice
+    if (Nq == 1) causal = 0;            // (assuming head-contiguous q and o when Nq > 1)
+    Nq *= Hq / Hk;
     Hq = Hk;
-    causal = 0;
   }
   if (block_m == 0 && block_n == 0) default_tile(Nq, d, causal, &block_m, &block_n);
   if (!tile_ok(d, block_m, block_n)) return 1;

@@ -115,7 +115,8 @@ fa_status fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, flo
  *             the one that differs from top-left only when the lengths differ): the
  *             last query sees every key. With Nq = Nk this is fa_fwd's mask. A query
  *             with no visible key (Nq > Nk, i < Nq - Nk) gets O = 0 and LSE = -inf.
- *   block_m, block_n: a compiled tile, or 0, 0 for the tile fa_fwd would choose for Nq.
+ *   block_m, block_n: a compiled tile, or 0, 0 for the tile fa_fwd would choose for Nq
+ *             (for the packed row count when grouped heads are packed, see below).
  *   Other arguments, ownership and errors as for fa_fwd; additionally
  *   FA_ERR_BAD_STRIDE. Nk = 0 is allowed (every row gets O = 0, LSE = -inf; k and v
  *   may then be NULL). B*Hq*Nq == 0 is a no-op.
@@ -148,9 +149,12 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
  *   Other arguments, results and errors as fa_fwd_ex; additionally FA_ERR_BAD_SPLITS
  *   and FA_ERR_WORKSPACE. The result equals fa_fwd_ex's up to rounding.
  *
- * With Nq = 1 and Hq > Hk (decoding with grouped K/V heads) fa_fwd_ex and fa_fwd_split
- * process the query heads that share a K/V head as the rows of one block, reading
- * each K/V head once; this needs nothing of the caller.
+ * With Hq > Hk and fewer than 64 query rows per head (decoding, a few draft tokens)
+ * fa_fwd_ex and fa_fwd_split process the query heads that share a K/V head as the
+ * rows of one slice, so that each K/V tile is read once for the whole group. With one
+ * row per head this holds for any layout; with more, q and o must be head-contiguous
+ * (head stride = Nq row strides, as in a contiguous [B, Hq, Nq, d]), and other
+ * layouts run unpacked. The results do not depend on it beyond rounding.
  */
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                        int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d,
@@ -164,9 +168,12 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
  * per range and query row; 0 if num_splits = 1 or an argument is out of range. */
 size_t fa_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d, int num_splits);
 
-/* A split count for fa_fwd_split (>= 1): the one that minimises the modelled time,
- * rounds of resident workgroups times key tiles per workgroup. block_m, block_n as in
- * fa_fwd_ex (0, 0: the default tile). 1 when the query blocks alone fill the GPU. */
+/* A split count for fa_fwd_split (>= 1): enough key ranges that query blocks times
+ * ranges fill the GPU's workgroup slots (two per compute unit for blocks at most half
+ * full, else as many as fit), at most one range per 8 key tiles and at most 256; 1 when
+ * the query blocks alone fill the GPU. Grouped heads with fewer than 64 rows count as
+ * packed (assuming head-contiguous q and o). block_m, block_n as in fa_fwd_ex (0, 0:
+ * the default tile). */
 int fa_split_default(int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, int causal,
                      int block_m, int block_n);
 

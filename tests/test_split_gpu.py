@@ -1,6 +1,6 @@
 """GPU parity of split-KV (fa_fwd_split, through the C ABI) and of decoding with grouped
-K/V heads (one query row per head, packed into one block per K/V head) against the
-fp64 CPU oracle.
+K/V heads (fewer than 64 query rows per head, the heads of a group packed into one
+slice per K/V head) against the fp64 CPU oracle.
 
 Tolerances as in test_parity_gpu.py (max |dO| <= 2e-3 fp16, <= 1e-2 bf16, max
 |dLSE| <= 1e-3). Split-KV computes the same attention: every key range's partial
@@ -176,3 +176,40 @@ def test_decode_grouped_heads_fwd_ex(layout, hq, hk):
             o, lse = fa.fwd_ex(qd, k.to(DEV), v.to(DEV), scale=1 / math.sqrt(d), causal=causal, out=out)
             torch.cuda.synchronize()
             _compare(o, lse, _reference(q, k, v, 1 / math.sqrt(d), causal), dtype, f"decode {layout}")
+
+
+_TILES = [(64, 64), (128, 64), (128, 32), (256, 32), (256, 64), (512, 32)]
+
+
+@pytest.mark.parametrize("nq,nk", [(2, 1500), (4, 1500), (7, 1500), (33, 1500), (63, 1500), (64, 1500), (33, 20)])
+@pytest.mark.parametrize("hq,hk", [(8, 2), (32, 8), (4, 1)])
+def test_decode_grouped_heads_several_rows(nq, nk, hq, hk):
+    """A few query rows per head (draft tokens) with grouped heads. With fewer than 64
+    rows and head-contiguous q and o the heads of a group are packed into one slice per
+    K/V head, and the bottom-right causal mask takes row mod Nq as the query index; 64
+    rows and the [B, N, H, d] layout run unpacked. Both against the oracle: unsplit
+    (default and every compiled tile), split-KV at the suggested count and at 5 ranges.
+    (33, 20) has causal rows that see no key."""
+    for d, dtype in ((64, "f16"), (128, "bf16")):
+        scale = 1 / math.sqrt(d)
+        q, k, v = _qkv(2, hq, hk, nq, nk, d, dtype, seed=nq * 7 + hq + hk + d + nk)
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        for causal in (False, True):
+            ref = _reference(q, k, v, scale, causal)
+            _say(f"[rows] nq={nq} nk={nk} hq={hq} hk={hk} d={d} causal={causal}")
+            o, lse = fa.fwd_ex(qd, kd, vd, scale=scale, causal=causal)
+            torch.cuda.synchronize()
+            _compare(o, lse, ref, dtype, f"rows nq={nq} default tile")
+            for bm, bn in _TILES:
+                if fa.fa_tile_supported(d, bm, bn):
+                    o, lse = fa.fwd_ex(qd, kd, vd, scale=scale, causal=causal, block_m=bm, block_n=bn)
+                    torch.cuda.synchronize()
+                    _compare(o, lse, ref, dtype, f"rows nq={nq} tile ({bm},{bn})")
+            for splits in (None, 5):
+                check_split(q, k, v, scale, causal, dtype, splits, label=f"rows nq={nq}", ref=ref)
+            # [B, N, H, d] storage: head stride d, not Nq rows, so the heads are not packed
+            qt = q.transpose(1, 2).contiguous().to(DEV).transpose(1, 2)
+            out = torch.empty((2, nq, hq, d), dtype=q.dtype, device=DEV).transpose(1, 2)
+            o, lse = fa.fwd_ex(qt, kd, vd, scale=scale, causal=causal, out=out)
+            torch.cuda.synchronize()
+            _compare(o, lse, ref, dtype, f"rows nq={nq} bnhd")
