@@ -108,3 +108,56 @@ def test_largest_key_count(d, dtype):
     del k, v
     torch.cuda.empty_cache()
 
+
+
+def test_backward_largest_key_count():
+    """fa_bwd_ex at the largest accepted key count (d = 128, bf16; with fp16 the weights
+    1/N_k ~ 1e-7 would be subnormal), 4 query heads of 64 rows over one K/V head,
+    against closed forms that hold at any size. Q = 0 makes every weight 1/N_k, so
+    dV_j = (1/N_k) sum of dO over the group's rows for every key, dK = 0 exactly, and
+    dQ_i = (s/N_k) sum_j (dO_i . (v_j - vbar)) k_j. K and V are periodic in j mod 7
+    (v_j as above, k_j[c] = ((2 j + 3 c) mod 7 - 3) / 4), so the sums over j are residue
+    counts."""
+    d, dtype, hq, nq = 128, "bf16", 4, 64
+    nk = _max_keys(d)
+    scale = 1 / math.sqrt(d)
+    print(f"[limits] backward d={d} {dtype} Nk={nk}", flush=True)
+    idx = torch.arange(nk, device=DEV) % 7
+    v7 = np.array([[((a + c) % 7 - 3) / 4 for c in range(d)] for a in range(7)])
+    k7 = np.array([[((2 * a + 3 * c) % 7 - 3) / 4 for c in range(d)] for a in range(7)])
+    v = torch.tensor(v7, dtype=torch.float32, device=DEV).to(TORCH_DT[dtype])[idx].reshape(1, 1, nk, d)
+    k = torch.tensor(k7, dtype=torch.float32, device=DEV).to(TORCH_DT[dtype])[idx].reshape(1, 1, nk, d)
+    del idx
+    q = torch.zeros((1, hq, nq, d), dtype=TORCH_DT[dtype], device=DEV)
+    g = torch.Generator("cpu").manual_seed(77)
+    do = torch.randn((1, hq, nq, d), generator=g).to(TORCH_DT[dtype])
+    o, lse = fa.fwd_split(q, k, v, scale=scale)
+    dq, dk, dv = fa.bwd_ex(q, k, v, o, do.to(DEV), lse, scale=scale)
+    torch.cuda.synchronize()
+    cnt = np.array([nk // 7 + (1 if a < nk % 7 else 0) for a in range(7)], dtype=np.float64)
+    vbar = (cnt[:, None] * v7).sum(0) / nk
+    # the forward on the way: O = mean of V, LSE = ln N_k
+    assert np.abs(o.float().cpu().double().numpy() - vbar).max() <= TOL_O[dtype]
+    assert np.abs(lse.cpu().double().numpy() - math.log(nk)).max() <= 1e-3
+    dod = do.double().numpy()[0]                                   # [hq, nq, d]
+    dv_ref = dod.sum(axis=(0, 1)) / nk                             # the same row for every key
+    ksum = (cnt[:, None] * k7).sum(0)
+    proj = np.einsum("hid,ad->hia", dod, v7)                       # dO_i . v7[a]
+    dq_ref = scale / nk * (np.einsum("hia,a,ad->hid", proj, cnt, k7) - (dod @ vbar)[..., None] * ksum)
+    assert torch.count_nonzero(dk) == 0
+    u = 2.0 ** -8
+    for name, got, ref in (("dq", dq[0].float().cpu().double().numpy(), dq_ref),
+                           ("dv", None, dv_ref)):
+        if name == "dv":
+            # every key's row: check the first, the last and a sample in between
+            rows = torch.tensor([0, 1, 2, 3, nk // 2, nk - 2, nk - 1], device=DEV)
+            got = dv[0, 0, rows].float().cpu().double().numpy()
+            ref = np.broadcast_to(ref, got.shape)
+            spread = (dv[0, 0].float().amax(dim=0) - dv[0, 0].float().amin(dim=0)).abs().max().item()
+            print(f"[limits]   dv spread over all keys {spread:.2e}", flush=True)
+            assert spread <= 8 * u * np.abs(ref).max()
+        ratio = np.abs(got - ref).max() / np.abs(ref).max()
+        print(f"[limits]   {name}: max|d|/max|ref| = {ratio:.2e} (bound {8 * u:.2e})", flush=True)
+        assert ratio <= 8 * u
+    del k, v, dk, dv
+    torch.cuda.empty_cache()
