@@ -98,9 +98,7 @@ __device__ __forceinline__ WorkItem work_item(const Params& p) {
   const int bh = w / per_slice;
   const int r = w - bh * per_slice;
   const int split = r / p.num_m_blocks;
-  int mb = r - split * p.num_m_blocks;
-  if (CAUSAL) mb = p.num_m_blocks - 1 - mb;
-  return {bh, split, mb};
+  return {bh, split, r - split * p.num_m_blocks};
 }
 
 // Base pointers of one (batch, query head) slice and of the K/V head it reads.
