@@ -281,18 +281,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   // Direct-to-LDS loads: load i of a tile fills LDS bytes [1024 i, 1024 i + 1024),
   // i.e. rows ROWS_PER_DMA*i.. of the tile; lane l fills tile row
   // ROWS_PER_DMA*i + 16 l / (2D), chunk position p = (16 l mod 2D) / 16, and so fetches
-  // source chunk p ^ swz(row). This wave issues loads i = NW kk + wave. K and V
-  // may have different row strides, so each has its own lane offsets.
-  uint32_t dma_off_k[DMA_PER_WAVE], dma_off_v[DMA_PER_WAVE];
+  // source chunk p ^ swz(row). This wave issues loads i = NW kk + wave, whose lane
+  // offsets depend on i only through i mod PATS = ((NW kk) mod PATS + wave) mod PATS:
+  // they are kept per value of (NW kk) mod PATS, a compile-time index (one or two
+  // registers per tensor, not one per load). K and V may have different row
+  // strides, so each has its own lane offsets.
+  uint32_t dma_off_k[PATS], dma_off_v[PATS];
 #pragma unroll
-  for (int kk = 0; kk < DMA_PER_WAVE; ++kk) {
-    const int i = kk * NW + wave;
+  for (int q = 0; q < PATS; ++q) {
     const int r_local = (16 * lane) / (2 * D);
     const int pch = ((16 * lane) % (2 * D)) / 16;
-    const int r = ROWS_PER_DMA * (i % PATS) + r_local;               // tile row mod 16
+    const int r = ROWS_PER_DMA * ((q + wave) % PATS) + r_local;        // tile row mod 16
     const int col = (pch ^ swz<D>(r)) << 3;
-    dma_off_k[kk] = (uint32_t)((r_local * p.k_sr + col) * 2);
-    dma_off_v[kk] = (uint32_t)((r_local * p.v_sr + col) * 2);
+    dma_off_k[q] = (uint32_t)((r_local * p.k_sr + col) * 2);
+    dma_off_v[q] = (uint32_t)((r_local * p.v_sr + col) * 2);
   }
   // The 2-wave tile serves decoding (one to a few query rows per K/V head) and short
   // sequences, where every K/V byte is read about once: its loads are non-temporal
@@ -300,12 +302,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   // 5.6 -> 6.4 at 64; neutral at d = 64, and 9-11% slower on the causal four-wave tiles,
   // whose K/V tiles are re-read from L2 by every row block).
   constexpr int LOAD_AUX = (NW == 2 && D == 128) ? 2 : 0;
-  auto issue_tile_load = [&](const __amdgpu_buffer_rsrc_t& rsrc, const uint32_t (&lane_off)[DMA_PER_WAVE], int sr,
+  auto issue_tile_load = [&](const __amdgpu_buffer_rsrc_t& rsrc, const uint32_t (&lane_off)[PATS], int sr,
                              short* dst, int n0) {
 #pragma unroll
     for (int kk = 0; kk < DMA_PER_WAVE; ++kk) {
       const int i = kk * NW + wave;
-      buffer_load16_to_lds<LOAD_AUX>(rsrc, dst + 512 * i, lane_off[kk], (uint32_t)((n0 + ROWS_PER_DMA * i) * sr * 2));
+      buffer_load16_to_lds<LOAD_AUX>(rsrc, dst + 512 * i, lane_off[(kk * NW) % PATS],
+                                     (uint32_t)((n0 + ROWS_PER_DMA * i) * sr * 2));
     }
   };
 
