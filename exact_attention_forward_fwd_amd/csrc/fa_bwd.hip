@@ -10,16 +10,16 @@
 // kernel of its own instead, Q-stationary like the forward: both kernels recompute
 // P from the LSE, so no atomics, no fp32 dQ buffer, and the result is deterministic.
 //
-// Three launches on the caller's stream:
-//   1. fa_bwd_delta_kernel: -D_i = -dO_i . O_i and the LSE in base-2 units
-//      (LSE_i log2 e, +inf for a row that sees no key), fp32, into the caller's
-//      workspace;
-//   2. fa_bwd_dq_kernel: a workgroup pins 128 query rows (4 waves x 32) with Q^T and
-//      dO^T in registers and streams K and V in tiles of 32 keys through LDS:
+// Two launches on the caller's stream:
+//   1. fa_bwd_dq_kernel: a workgroup pins 128 query rows (4 waves x 32) with Q^T and
+//      dO^T in registers, forms D_i = dO_i . O_i and the LSE in base-2 units
+//      (LSE_i log2 e, +inf for a row that sees no key) of its rows and leaves -D and
+//      that LSE, fp32, in the caller's workspace; then it streams K and V in tiles of
+//      32 keys through LDS:
 //        S^T = K Q^T, dP^T = V dO^T            (MFMA, K and V rows from LDS)
 //        P^T = 2^(c S^T - LSE log2 e), dS^T = P^T * (dP^T - D)   (VALU)
 //        dQ^T += K^T dS^T                      (MFMA, K^T by transposing LDS reads)
-//   3. fa_bwd_dkdv_kernel: a workgroup pins 128 keys (4 waves x 32) with K^T and V^T
+//   2. fa_bwd_dkdv_kernel: a workgroup pins 128 keys (4 waves x 32) with K^T and V^T
 //      in registers (V in LDS at d = 128) and streams Q, dO, LSE and -D in tiles of
 //      32 query rows:
 //        S = Q K^T, dP - D = dO V^T - D        (MFMA, Q and dO rows from LDS; the
@@ -73,29 +73,6 @@ __device__ __forceinline__ float to_f32(short x) {
 
 // ---- 1. D_i = dO_i . O_i -------------------------------------------------------------
 // D / 8 lanes per row, 8 elements (16 bytes) each, then a butterfly sum.
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void fa_bwd_delta_kernel(BwdParams p) {
-  constexpr int LPR = D / 8;
-  constexpr int RPB = 256 / LPR;
-  const int64_t rows = (int64_t)p.slices_q * p.Nq;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int j = threadIdx.x % LPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const i16x8 a = *(const i16x8*)(p.dout + row * D + 8 * j);
-    const i16x8 b = *(const i16x8*)(p.o + row * D + 8 * j);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(to_f32<BF16>(a[e]), to_f32<BF16>(b[e]), acc);
-  }
-#pragma unroll
-  for (int w = LPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, LPR);
-  if (row < rows && j == 0) {
-    p.nd[row] = -acc;
-    const float lse = p.lse[row];
-    p.l2[row] = lse == -INFINITY ? INFINITY : lse * kLog2e;
-  }
-}
-
 // Work item of a workgroup out of T: slice and block of 128 rows (queries for dQ,
 // keys for dK/dV). Contiguous ranges per XCD, so the blocks of one slice share an L2.
 //
@@ -259,11 +236,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     qf[ks] = buffer_load16(rq, (uint32_t)((qrow * D + ks * 16 + 8 * hi) * 2));
     dof[ks] = buffer_load16(rdo, (uint32_t)((qrow * D + ks * 16 + 8 * hi) * 2));
   }
-  // this lane's query: LSE in log2 units and D (rows past Nq, or seeing no key at
-  // all: +inf, no weight)
+  // This lane's query: D = dO . O, the row sum that dS = P (dP - D) needs, and the
+  // LSE in log2 units (+inf, i.e. no weight, for a row that sees no key or lies past
+  // Nq). Lanes l32 and l32 + 32 hold the row's columns 16 ks + 8 hi .. +7: each sums
+  // its own and the two halves are added. Both values also go to the workspace for
+  // the dK/dV kernel, which runs after this one on the same stream.
   const bool live = qrow < Nq;
-  const float lse2 = live ? p.l2[(int64_t)bh * Nq + qrow] : INFINITY;
-  const float dl = live ? -p.nd[(int64_t)bh * Nq + qrow] : 0.f;
+  float dpart = 0.f;
+  {
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + base, p.q_bytes);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const i16x8 of = buffer_load16(ro, (uint32_t)((qrow * D + ks * 16 + 8 * hi) * 2));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf(to_f32<BF16>(dof[ks][e]), to_f32<BF16>(of[e]), dpart);
+    }
+  }
+  const float dsum = sum_halves(dpart);
+  const float lse_nat = live ? p.lse[(int64_t)bh * Nq + qrow] : -INFINITY;
+  const float lse2 = lse_nat == -INFINITY ? INFINITY : lse_nat * kLog2e;
+  const float dl = live ? dsum : 0.f;
+  if (live && hi == 0) {
+    p.nd[(int64_t)bh * Nq + qrow] = -dsum;
+    p.l2[(int64_t)bh * Nq + qrow] = lse2;
+  }
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -614,10 +610,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 template <int D, bool BF16>
 hipError_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) {
-  constexpr int RPB = 256 / (D / 8);
-  const int64_t rows = (int64_t)p.slices_q * p.Nq;
-  if (rows > 0)
-    hipLaunchKernelGGL((fa_bwd_delta_kernel<D, BF16>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, s, p);
+  // the dQ kernel writes -D and the base-2 LSE of every query row before the dK/dV
+  // kernel reads them (stream order); both grids are empty only without rows or keys
   if (causal) {
     if (p.dq_wgs > 0) hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, true>), dim3(p.dq_wgs), dim3(256), 0, s, p);
     if (p.dkdv_wgs > 0) hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, true>), dim3(p.dkdv_wgs), dim3(256), 0, s, p);
