@@ -610,8 +610,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 template <int D, bool BF16>
 hipError_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) {
-  // the dQ kernel writes -D and the base-2 LSE of every query row before the dK/dV
-  // kernel reads them (stream order); both grids are empty only without rows or keys
+  // The dQ kernel writes -D and the base-2 LSE of every query row before the dK/dV
+  // kernel reads them (stream order). dq_wgs is 0 only without query rows, dkdv_wgs
+  // only without keys.
   if (causal) {
     if (p.dq_wgs > 0) hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, true>), dim3(p.dq_wgs), dim3(256), 0, s, p);
     if (p.dkdv_wgs > 0) hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, true>), dim3(p.dkdv_wgs), dim3(256), 0, s, p);
