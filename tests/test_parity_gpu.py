@@ -123,36 +123,29 @@ def test_zero_query_closed_form(N, d, dtype):
 
 # --- the five workloads ----------------------------------------------------------------
 
-def _sample_rows(w, spikes, per_head=256, seed=0):
-    """Row sample for the largest workload: every spiked row, the first and last 64
-    rows of each (b, h) slice and per_head random rows."""
-    rng = np.random.default_rng(seed)
-    rows = []
-    for b in range(w.B):
-        for h in range(w.H):
-            base = (b * w.H + h) * w.N
-            picked = set(spikes[b, h].tolist()) if spikes.numel() else set()
-            picked.update(range(64))
-            picked.update(range(w.N - 64, w.N))
-            picked.update(rng.choice(w.N, per_head, replace=False).tolist())
-            rows.extend(base + i for i in sorted(picked))
-    return np.array(rows, dtype=np.int64)
+def _spiked_rows(w, spikes):
+    """Flat row indices of the rows scaled x20 in every (b, h) slice."""
+    return np.array(sorted((b * w.H + h) * w.N + int(i) for b in range(w.B) for h in range(w.H)
+                           for i in spikes[b, h].tolist()), dtype=np.int64)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
 def test_workload_full_oracle(idx):
+    """Every row of every workload against the full oracle, in the launch configuration
+    the benchmark times. For the N = 16384 workload (about 20 s of host time) the
+    spiked rows, whose running maximum jumps and forces the alpha rescaling, are also
+    reported on their own."""
     w = WORKLOADS[idx]
-    q, k, v, _ = make_inputs(w)
-    check_against_oracle(q, k, v, w.scale, w.causal, w.dtype, tile=w.tile, label=w.name)
-
-
-def test_workload_4_sampled_rows():
-    w = WORKLOADS[4]
     q, k, v, spikes = make_inputs(w)
-    rows = _sample_rows(w, spikes)
-    o, lse = check_against_oracle(q, k, v, w.scale, w.causal, w.dtype, rows=rows, label=w.name)
-    # every row: O lies in V's range [-1, 1] and LSE is finite
-    assert np.all(np.abs(o) <= 1.0) and np.all(np.isfinite(lse))
+    _say(f"[parity] {w.name}: full oracle over {w.B * w.H * w.N} rows")
+    o, lse = check_against_oracle(q, k, v, w.scale, w.causal, w.dtype, tile=w.tile, label=w.name)
+    if spikes.numel():
+        rows = _spiked_rows(w, spikes)
+        o_ref, lse_ref = oracle.attention_rows(f64(q), f64(k), f64(v), w.scale, w.causal, rows)
+        err_o = np.abs(o.reshape(-1, w.d)[rows] - o_ref).max()
+        err_l = np.abs(lse.reshape(-1)[rows] - lse_ref).max()
+        _say(f"[parity]   spiked rows ({rows.size}): max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+        assert err_o <= TOL_O[w.dtype] and err_l <= TOL_LSE
 
 
 def test_workload_1_default_tile_matches_forced():
