@@ -19,9 +19,12 @@ STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_UNSUPPORTED_HEADDIM",
     4: "FA_ERR_BAD_SCALE", 5: "FA_ERR_BAD_DTYPE", 6: "FA_ERR_MISALIGNED", 7: "FA_ERR_TOO_LARGE",
     8: "FA_ERR_UNSUPPORTED_TILE", 9: "FA_ERR_HIP", 10: "FA_ERR_BAD_STRIDE", 11: "FA_ERR_BAD_SPLITS",
-    12: "FA_ERR_WORKSPACE",
+    12: "FA_ERR_WORKSPACE", 13: "FA_ERR_SCRATCH_LIMIT",
 }
-EXPORTED = ("fa_fwd", "fa_fwd_tiled", "fa_fwd_ex", "fa_fwd_split", "fa_split_workspace_bytes", "fa_split_default",
+# size of the per-GPU scratch array of fa_fwd_split_noalloc (FA_SPLIT_SCRATCH_BYTES in fa.h)
+SPLIT_SCRATCH_BYTES = 64 << 20
+EXPORTED = ("fa_fwd", "fa_fwd_tiled", "fa_fwd_ex", "fa_fwd_split", "fa_fwd_split_noalloc", "fa_split_workspace_bytes",
+            "fa_split_default",
             "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes", "fa_tile_supported", "fa_default_tile", "fa_status_str")
 
 
@@ -56,6 +59,9 @@ def load_library(path: str = LIB_PATH):
     lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p,
                                  ctypes.c_float, i32, i32, vp, i32, i32, i32, vp, ctypes.c_size_t]
     lib.fa_fwd_split.restype = i32
+    lib.fa_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64p, i64p, i64p, i64p,
+                                         ctypes.c_float, i32, i32, vp, i32, i32, i32]
+    lib.fa_fwd_split_noalloc.restype = i32
     lib.fa_split_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
     lib.fa_split_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_split_default.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, i32]
@@ -115,6 +121,15 @@ def fa_fwd_split(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, q_strides, k_strides, v_
                                        _strides(k_strides), _strides(v_strides), _strides(o_strides),
                                        scale, int(causal), dtype, stream, int(block_m), int(block_n),
                                        int(num_splits), workspace, int(workspace_bytes))
+
+
+def fa_fwd_split_noalloc(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, q_strides, k_strides, v_strides, o_strides,
+                         scale, causal, dtype, stream, block_m, block_n, num_splits) -> int:
+    """Raw C call of the split-KV entry point that uses the library's built-in scratch."""
+    return load_library().fa_fwd_split_noalloc(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, _strides(q_strides),
+                                               _strides(k_strides), _strides(v_strides), _strides(o_strides),
+                                               scale, int(causal), dtype, stream, int(block_m), int(block_n),
+                                               int(num_splits))
 
 
 def fa_split_workspace_bytes(B: int, Hq: int, Nq: int, d: int, num_splits: int) -> int:
@@ -309,6 +324,25 @@ def fwd_split(q, k, v, scale: float | None = None, causal: bool = False, num_spl
                       float(scale), causal, _dtype_code(q), sp, bm, bn, num_splits, ws_ptr, ws_bytes)
     if st != 0:
         raise FaError(st, "fa_fwd_split")
+    return out, lse
+
+
+def fwd_split_noalloc(q, k, v, scale: float | None = None, causal: bool = False, num_splits: int | None = None,
+                      block_m: int | None = None, block_n: int | None = None, out=None, lse=None, stream=None):
+    """fwd_split through fa_fwd_split_noalloc: the partials go to the library's per-GPU
+    scratch array instead of a workspace. With ``out`` and ``lse`` given, nothing is
+    allocated on the device by this call (the C entry point never allocates)."""
+    scale, out, lse, sp = _general_args(q, k, v, scale, out, lse, stream)
+    B, Hq, Nq, d = q.shape
+    Hk, Nk = k.shape[1], k.shape[2]
+    bm, bn = block_m or 0, block_n or 0
+    if num_splits is None:
+        num_splits = fa_split_default(B, Hq, Hk, Nq, Nk, d, causal, bm, bn)
+    st = fa_fwd_split_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
+                              Hk, Nq, Nk, d, q.stride()[:3], k.stride()[:3], v.stride()[:3], out.stride()[:3],
+                              float(scale), causal, _dtype_code(q), sp, bm, bn, num_splits)
+    if st != 0:
+        raise FaError(st, "fa_fwd_split_noalloc")
     return out, lse
 
 

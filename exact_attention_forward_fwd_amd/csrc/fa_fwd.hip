@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+#include <mutex>
 #include <type_traits>
 
 #include "fa.h"
@@ -1151,6 +1152,34 @@ int split_heuristic(int64_t B, int64_t Hq, int64_t Nq, int64_t Nk, int64_t d, in
   return sp < 1 ? 1 : (int)sp;
 }
 
+// ------------------------------------------------------------------------------------
+// Built-in scratch for the allocation-free split-KV entry point
+// ------------------------------------------------------------------------------------
+//
+// One array per GPU, as large as the biggest split-KV partial set this entry point
+// accepts; it lives until the process ends. Host code never passes the array's name
+// to a kernel (on the host it only stands for the symbol): its device address is
+// looked up once per device, with that device current, and kept here.
+constexpr size_t kScratchBytes = FA_SPLIT_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array, or null on a HIP error.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 // Everything fa_fwd, fa_fwd_ex and fa_fwd_split share. num_splits = 1: one workgroup
 // per query block, written straight to o and lse; otherwise partials in workspace
 // and a merge launch.
@@ -1158,7 +1187,7 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
               int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, const int64_t* qs_in, const int64_t* ks_in,
               const int64_t* vs_in, const int64_t* os_in, float scale, int causal, fa_dtype dtype,
               void* stream, int bm, int bn, int num_splits = 1, void* workspace = nullptr,
-              size_t workspace_bytes = 0) {
+              size_t workspace_bytes = 0, bool use_scratch = false) {
   if (B < 0 || Hq < 0 || Hk < 0 || Nq < 0 || Nk < 0) return FA_ERR_BAD_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_BAD_SCALE;
@@ -1222,6 +1251,13 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (splits > 1) {
     const int64_t rows = slices * Nq;
     const uint64_t need = (uint64_t)splits * rows * (d + 1) * 4;
+    if (use_scratch) {
+      // the built-in scratch: looked up only once every argument has passed
+      if (need > kScratchBytes) return FA_ERR_SCRATCH_LIMIT;
+      workspace = device_scratch();
+      if (!workspace) return FA_ERR_HIP;
+      workspace_bytes = kScratchBytes;
+    }
     if (!workspace || ((uintptr_t)workspace & 15) || workspace_bytes < need) return FA_ERR_WORKSPACE;
     po = (float*)workspace;
     plse = po + splits * rows * d;
@@ -1314,6 +1350,21 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
              causal, dtype, stream, block_m, block_n, num_splits, workspace, workspace_bytes);
 }
 
+fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                               int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d,
+                               const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
+                               const int64_t* o_strides, float scale, int causal, fa_dtype dtype, void* stream,
+                               int block_m, int block_n, int num_splits) {
+  // the partials of num_splits ranges must fit the built-in scratch: the same bound as
+  // the workspace size of the caller-workspace form, checked before any HIP call
+  if (num_splits > 1 && B > 0 && Hq > 0 && Nq > 0 && (d == 64 || d == 128) && num_splits <= kMaxSplits) {
+    const double need = (double)num_splits * (double)B * (double)Hq * (double)Nq * (double)(d + 1) * 4.0;
+    if (need > (double)kScratchBytes) return FA_ERR_SCRATCH_LIMIT;
+  }
+  return run(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, q_strides, k_strides, v_strides, o_strides, scale, causal,
+             dtype, stream, block_m, block_n, num_splits, nullptr, 0, true);
+}
+
 size_t fa_split_workspace_bytes(int64_t B, int64_t Hq, int64_t Nq, int64_t d, int num_splits) {
   if (B <= 0 || Hq <= 0 || Nq <= 0 || (d != 64 && d != 128) || num_splits < 1 || num_splits > kMaxSplits) return 0;
   if (num_splits == 1) return 0;
@@ -1359,6 +1410,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_BAD_STRIDE: return "strides must be non-negative multiples of 8 elements, row stride >= d";
     case FA_ERR_BAD_SPLITS: return "num_splits must be between 1 and 256";
     case FA_ERR_WORKSPACE: return "split-KV workspace missing, not 16-byte aligned or smaller than fa_split_workspace_bytes";
+    case FA_ERR_SCRATCH_LIMIT: return "split-KV partials exceed the built-in scratch (FA_SPLIT_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -48,8 +48,12 @@ typedef enum {
   FA_ERR_HIP = 9,                /* the HIP runtime reported an error at launch */
   FA_ERR_BAD_STRIDE = 10,        /* a stride is negative or not a multiple of 8 elements, or a row stride < d */
   FA_ERR_BAD_SPLITS = 11,        /* num_splits outside [1, 256] */
-  FA_ERR_WORKSPACE = 12          /* workspace (split-KV or backward) NULL, not 16-byte aligned or too small */
+  FA_ERR_WORKSPACE = 12,         /* workspace (split-KV or backward) NULL, not 16-byte aligned or too small */
+  FA_ERR_SCRATCH_LIMIT = 13      /* fa_fwd_split_noalloc: the partials exceed FA_SPLIT_SCRATCH_BYTES */
 } fa_status;
+
+/* Size of the per-GPU scratch array fa_fwd_split_noalloc uses (64 MiB). */
+#define FA_SPLIT_SCRATCH_BYTES ((size_t)64 << 20)
 
 /*
  * fa_fwd — exact attention forward, asynchronous on `stream`.
@@ -163,6 +167,33 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        float scale, int causal, fa_dtype dtype, void* stream,
                        int block_m, int block_n, int num_splits, void* workspace,
                        size_t workspace_bytes);
+
+/*
+ * fa_fwd_split_noalloc — fa_fwd_split without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc. The partials go to a scratch array that the library
+ * holds in each GPU's memory (FA_SPLIT_SCRATCH_BYTES, 64 MiB, allocated when the
+ * library's code is loaded on that GPU and kept until the process ends); the call itself
+ * allocates and frees nothing. Its device address is looked up on the first call on a
+ * device (the device current at the call, which must be the device of `stream`).
+ *
+ *   Arguments, results and other errors as fa_fwd_split with num_splits ranges.
+ *   FA_ERR_SCRATCH_LIMIT (nothing launched) when fa_split_workspace_bytes(B, Hq, Nq,
+ *   d, num_splits) exceeds FA_SPLIT_SCRATCH_BYTES; FA_ERR_HIP if the scratch address
+ *   cannot be obtained. num_splits = 1 does not touch the scratch.
+ *
+ * The scratch array is shared by every call on a GPU and holds the last call's
+ * partials; no contents need clearing between calls (every range writes its partials
+ * before the merge reads them). Calls that overlap on one GPU (different streams, or
+ * different host threads without ordering) race on it and give wrong results:
+ * serialise them, or use fa_fwd_split with separate workspaces.
+ */
+fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d,
+                               const int64_t* q_strides, const int64_t* k_strides,
+                               const int64_t* v_strides, const int64_t* o_strides,
+                               float scale, int causal, fa_dtype dtype, void* stream,
+                               int block_m, int block_n, int num_splits);
 
 /* Workspace bytes fa_fwd_split needs for these sizes and num_splits: 4 (d + 1) bytes
  * per range and query row; 0 if num_splits = 1 or an argument is out of range. */

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(13):
+    for code in range(14):
         s = fa.status_str(code)
         assert s and s != "unknown status"
     assert fa.status_str(99) == "unknown status"
@@ -186,3 +186,20 @@ def test_product_path_does_not_reference_the_oracle():
 def test_missing_library_raises(tmp_path):
     with pytest.raises(RuntimeError):
         fa.load_library(str(tmp_path / "libfa.so"))
+
+
+def test_noalloc_split_refuses_partials_beyond_the_scratch():
+    """fa_fwd_split_noalloc checks the partials' size against the built-in scratch
+    before any HIP call: one range more than fits is refused, nothing is launched."""
+    d, rows = 128, 8 * 1024                       # B * Hq * Nq query rows
+    per_range = rows * (d + 1) * 4
+    fits = fa.SPLIT_SCRATCH_BYTES // per_range
+    assert fa.fa_split_workspace_bytes(1, 8, 1024, d, fits) <= fa.SPLIT_SCRATCH_BYTES
+    st = fa.fa_fwd_split_noalloc(A, A, A, A, A, 1, 8, 8, 1024, 4096, d, None, None, None, None, 0.088, 0, 1,
+                                 None, 0, 0, fits + 1)
+    assert st == 13 and "scratch" in fa.status_str(st)
+    # the other checks are those of fa_fwd_split (nothing launched either)
+    assert fa.fa_fwd_split_noalloc(A, A, A, A, A, 1, 8, 8, 1024, 4096, 96, None, None, None, None, 0.088, 0, 1,
+                                   None, 0, 0, 4) == 3
+    assert fa.fa_fwd_split_noalloc(A, A, A, A, A, 1, 8, 8, 1024, 4096, d, None, None, None, None, 0.088, 0, 1,
+                                   None, 0, 0, 257) == 11
