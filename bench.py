@@ -247,10 +247,11 @@ def time_split(w, steps, warmup):
 
 
 def time_backward(w, steps, warmup):
-    """Per-call device time of fa_bwd (row sums, dQ kernel, dK/dV kernel) on a forward
-    benchmark workload with dO ~ N(0, 1), o and lse from fa_fwd. Algorithmic FLOPs are
-    the five products of the gradient (S, dP, dV, dK, dQ: 2.5x the forward's); the
-    kernels execute seven (S and dP once more in the dQ kernel)."""
+    """Per-call device time of fa_bwd (two launches: the dQ kernel, which also forms the
+    row terms D = dO.O and the base-2 LSE, then the dK/dV kernel) on a forward benchmark
+    workload with dO ~ N(0, 1), o and lse from fa_fwd. Algorithmic FLOPs are the five
+    products of the gradient (S, dP, dV, dK, dQ: 2.5x the forward's); the kernels
+    execute seven (S and dP once more in the dQ kernel)."""
     import torch
     import exact_attention_forward_fwd_amd as fa
     from exact_attention_forward_fwd_amd.workloads import make_inputs
@@ -287,6 +288,18 @@ def time_backward(w, steps, warmup):
                          "executed_flop": 3.5 * w.flops}}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_backward(w, budget_s=6.0):
     """The fp64 oracle's backward on whole (b, h) slices of the workload until the budget
     is spent (at least one slice), priced at the same algorithmic FLOPs."""
@@ -310,7 +323,8 @@ def cpu_baseline_backward(w, budget_s=6.0):
             break
     dt = time.perf_counter() - t0
     alg = 2.5 * w.flops / (w.B * w.H) * slices
-    return {"value": alg / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": alg / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"{slices} of {w.B * w.H} (batch, head) slices of {w.label()}, every gradient, fp64 C "
                       f"oracle backward, {dt:.1f} s"}
 
@@ -336,7 +350,7 @@ def cpu_baseline(w, budget_s=12.0):
     dt = time.perf_counter() - t0
     flops = w.flops / (w.B * w.H) * slices
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{slices} of {w.B * w.H} (batch, head) slices of {w.label()}, every row, "
                       f"fp64 three-pass C oracle, {dt:.1f} s"}
 

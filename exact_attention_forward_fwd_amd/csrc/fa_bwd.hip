@@ -269,8 +269,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 
   const int n_end = CAUSAL ? max(0, min(Nk, m0 + BM + off)) : Nk;
   const int ntiles = (n_end + BN - 1) / BN;
-  int n_full = (CAUSAL ? max(0, min(Nk, m0 + 1 + off)) : Nk) / BN;   // tiles visible to every query here
-  if (n_full > ntiles) n_full = ntiles;
 
   auto sync_tile = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -611,7 +609,7 @@ hipError_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) {
 // Hq / Hk query heads, Nq queries against Nk keys (causal: bottom-right alignment).
 fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                   void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d,
-                  float scale, int causal, fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                  float scale, int causal, fa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (B < 0 || Hq < 0 || Hk < 0 || Nq < 0 || Nk < 0) return FA_ERR_BAD_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_BAD_SCALE;
@@ -658,7 +656,7 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
   p.dkdv_wgs = (int)(B * Hk * kblocks);
   p.c = (float)((double)scale * 1.4426950408889634);
   p.scale = scale;
-  const hipStream_t s = (hipStream_t)stream;
+  const hipStream_t s = stream;
   const bool bf16 = dtype == FA_BF16;
   hipError_t e;
   if (d == 64) e = bf16 ? launch_bwd<64, true>(p, causal != 0, s) : launch_bwd<64, false>(p, causal != 0, s);
@@ -677,7 +675,7 @@ size_t fa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N) {
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                  void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
-                 fa_dtype dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                 fa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H, N, N, d, scale, causal, dtype, workspace,
                  workspace_bytes, stream);
 }
@@ -685,7 +683,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
 fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                     void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk,
                     int64_t d, float scale, int causal, fa_dtype dtype, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+                    hipStream_t stream) {
   return run_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hk, Nq, Nk, d, scale, causal, dtype, workspace,
                  workspace_bytes, stream);
 }

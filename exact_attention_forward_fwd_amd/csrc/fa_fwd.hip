@@ -1186,7 +1186,7 @@ void* device_scratch() {
 fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t Hq,
               int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, const int64_t* qs_in, const int64_t* ks_in,
               const int64_t* vs_in, const int64_t* os_in, float scale, int causal, fa_dtype dtype,
-              void* stream, int bm, int bn, int num_splits = 1, void* workspace = nullptr,
+              hipStream_t stream, int bm, int bn, int num_splits = 1, void* workspace = nullptr,
               size_t workspace_bytes = 0, bool use_scratch = false) {
   if (B < 0 || Hq < 0 || Hk < 0 || Nq < 0 || Nk < 0) return FA_ERR_BAD_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
@@ -1289,7 +1289,7 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
   p.c = (float)((double)scale * 1.4426950408889634);  // s * log2(e), rounded once
   p.po = po;
   p.plse = plse;
-  const hipStream_t s = (hipStream_t)stream;
+  const hipStream_t s = stream;
   const bool bf16 = dtype == FA_BF16;
   hipError_t e = (d == 64) ? launch_d<64>(p, bf16, causal != 0, bm, bn, s)
                            : launch_d<128>(p, bf16, causal != 0, bm, bn, s);
@@ -1318,7 +1318,7 @@ extern "C" {
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                  int64_t H, int64_t N, int64_t d, float scale, int causal, fa_dtype dtype,
-                 void* stream) {
+                 hipStream_t stream) {
   int bm, bn;
   default_tile(N, d, causal, &bm, &bn);
   return run(q, k, v, o, lse, B, H, H, N, N, d, nullptr, nullptr, nullptr, nullptr, scale, causal, dtype,
@@ -1327,7 +1327,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 fa_status fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                        int64_t H, int64_t N, int64_t d, float scale, int causal, fa_dtype dtype,
-                       void* stream, int block_m, int block_n) {
+                       hipStream_t stream, int block_m, int block_n) {
   if (block_m == 0 && block_n == 0) block_m = -1;   // no automatic choice here: (0, 0) is not a tile
   return run(q, k, v, o, lse, B, H, H, N, N, d, nullptr, nullptr, nullptr, nullptr, scale, causal, dtype,
              stream, block_m, block_n);
@@ -1336,7 +1336,7 @@ fa_status fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, flo
 fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                     int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, const int64_t* q_strides,
                     const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
-                    float scale, int causal, fa_dtype dtype, void* stream, int block_m, int block_n) {
+                    float scale, int causal, fa_dtype dtype, hipStream_t stream, int block_m, int block_n) {
   return run(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, q_strides, k_strides, v_strides, o_strides, scale,
              causal, dtype, stream, block_m, block_n);
 }
@@ -1344,7 +1344,7 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                        int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d, const int64_t* q_strides,
                        const int64_t* k_strides, const int64_t* v_strides, const int64_t* o_strides,
-                       float scale, int causal, fa_dtype dtype, void* stream, int block_m, int block_n,
+                       float scale, int causal, fa_dtype dtype, hipStream_t stream, int block_m, int block_n,
                        int num_splits, void* workspace, size_t workspace_bytes) {
   return run(q, k, v, o, lse, B, Hq, Hk, Nq, Nk, d, q_strides, k_strides, v_strides, o_strides, scale,
              causal, dtype, stream, block_m, block_n, num_splits, workspace, workspace_bytes);
@@ -1353,7 +1353,7 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
 fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                                int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d,
                                const int64_t* q_strides, const int64_t* k_strides, const int64_t* v_strides,
-                               const int64_t* o_strides, float scale, int causal, fa_dtype dtype, void* stream,
+                               const int64_t* o_strides, float scale, int causal, fa_dtype dtype, hipStream_t stream,
                                int block_m, int block_n, int num_splits) {
   // the partials of num_splits ranges must fit the built-in scratch: the same bound as
   // the workspace size of the caller-workspace form, checked before any HIP call
@@ -1395,7 +1395,7 @@ fa_status fa_default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal
   return FA_OK;
 }
 
-const char* fa_status_str(int status) {
+const char* fa_status_str(fa_status status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL_PTR: return "null pointer";

@@ -29,6 +29,10 @@
 extern "C" {
 #endif
 
+/* HIP's stream handle, declared exactly as the HIP runtime headers declare it, so that
+ * this header needs none of them (a repeated identical typedef is valid C and C++). */
+typedef struct ihipStream_t* hipStream_t;
+
 /* Element type of Q, K, V and O. */
 typedef enum {
   FA_F16 = 0,  /* IEEE binary16 */
@@ -73,7 +77,7 @@ typedef enum {
  *   dtype   : FA_F16 or FA_BF16. Scores, softmax state and accumulators are fp32;
  *             the softmax weights are rounded to `dtype` (round-to-nearest-even)
  *             for the P·V product and O is rounded to `dtype` at the end.
- *   stream  : a hipStream_t (NULL = the default stream).
+ *   stream  : the HIP stream to enqueue on (NULL = the default stream).
  *
  * Ownership: the caller allocates and frees every buffer. The library allocates
  * nothing, keeps no state between calls and does not synchronise; the call
@@ -84,17 +88,20 @@ typedef enum {
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                  int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
-                 fa_dtype dtype, void* stream);
+                 fa_dtype dtype, hipStream_t stream);
 
 /*
  * fa_fwd_tiled — fa_fwd with an explicit tile shape: block_m query rows per
- * workgroup and block_n keys per K/V tile (fa_fwd picks these itself). Used for
- * testing and tuning. Supported shapes are reported by fa_tile_supported; any
- * other pair returns FA_ERR_UNSUPPORTED_TILE without launching.
+ * workgroup and block_n keys per K/V tile (fa_fwd picks these itself). The tile is
+ * the blocking of "用 CuTe 读懂 FlashAttention" (its opening example fixes
+ * BlockM = BlockN = 64: one thread block per 64 query rows walking K/V in blocks of
+ * 64 keys); the 128-row single-head workload names that tile. Used for testing and
+ * tuning. Supported shapes are reported by fa_tile_supported; any other pair returns
+ * FA_ERR_UNSUPPORTED_TILE without launching.
  */
 fa_status fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, float* lse,
                        int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
-                       fa_dtype dtype, void* stream, int block_m, int block_n);
+                       fa_dtype dtype, hipStream_t stream, int block_m, int block_n);
 
 /*
  * fa_fwd_ex — the general form of fa_fwd, asynchronous on `stream`: unequal query and
@@ -129,7 +136,7 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float*
                     int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d,
                     const int64_t* q_strides, const int64_t* k_strides,
                     const int64_t* v_strides, const int64_t* o_strides,
-                    float scale, int causal, fa_dtype dtype, void* stream,
+                    float scale, int causal, fa_dtype dtype, hipStream_t stream,
                     int block_m, int block_n);
 
 /*
@@ -164,7 +171,7 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d,
                        const int64_t* q_strides, const int64_t* k_strides,
                        const int64_t* v_strides, const int64_t* o_strides,
-                       float scale, int causal, fa_dtype dtype, void* stream,
+                       float scale, int causal, fa_dtype dtype, hipStream_t stream,
                        int block_m, int block_n, int num_splits, void* workspace,
                        size_t workspace_bytes);
 
@@ -192,7 +199,7 @@ fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void
                                int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, int64_t d,
                                const int64_t* q_strides, const int64_t* k_strides,
                                const int64_t* v_strides, const int64_t* o_strides,
-                               float scale, int causal, fa_dtype dtype, void* stream,
+                               float scale, int causal, fa_dtype dtype, hipStream_t stream,
                                int block_m, int block_n, int num_splits);
 
 /* Workspace bytes fa_fwd_split needs for these sizes and num_splits: 4 (d + 1) bytes
@@ -236,7 +243,7 @@ int fa_split_default(int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
                  int64_t d, float scale, int causal, fa_dtype dtype, void* workspace,
-                 size_t workspace_bytes, void* stream);
+                 size_t workspace_bytes, hipStream_t stream);
 
 /*
  * fa_bwd_ex — fa_bwd for grouped K/V heads and unequal lengths, as fa_fwd_ex computes
@@ -251,7 +258,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
 fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hk,
                     int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, fa_dtype dtype,
-                    void* workspace, size_t workspace_bytes, void* stream);
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes fa_bwd needs: 8 per query row (B * H * N * 8); 0 for an empty or
  * negative size. For fa_bwd_ex pass H = Hq and N = Nq. */
@@ -266,7 +273,7 @@ fa_status fa_default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal
                           int* block_m, int* block_n);
 
 /* Static description of a status code. Never NULL. */
-const char* fa_status_str(int status);
+const char* fa_status_str(fa_status status);
 
 #ifdef __cplusplus
 }
