@@ -261,16 +261,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
         vo[db][sec] = r * D + ((ch ^ swz<D>(r)) << 3) + 4 * (ln & 1);
       }
   };
-  // The offsets normally stay in registers for the whole loop. In the two d = 128
-  // variants whose loop otherwise spills (causal with 64-key tiles, non-causal with
-  // 32-key tiles; the accumulators, Q^T and the previous tile's weights take most
-  // of 256 registers) they are recomputed where they are used (one XOR and shift
-  // each) from a copy of the lane index the compiler cannot hoist out of the loop.
-  // Measured: 449 -> 775 and 878 -> 1075 TFLOP/s; the other variants do not spill
-  // in their main loop and only lose by the extra VALU work. The non-causal 64-key
-  // variant recomputes them in its masked tiles (the ragged last tile) only, where
-  // the mask's registers made it spill (N = 1000, B = 8, H = 32: 683 -> 825 TFLOP/s).
-  constexpr bool RECOMPUTE_OFFSETS = D == 128 && ((CAUSAL && BN == 64) || (!CAUSAL && BN == 32));
+  // The offsets normally stay in registers for the whole loop. In the d = 128 causal
+  // variant, whose loop otherwise spills (the accumulators, Q^T and the previous
+  // tile's weights take most of 256 registers), they are recomputed where they are
+  // used (one XOR and shift each) from a copy of the lane index the compiler cannot
+  // hoist out of the loop (measured 449 -> 775 TFLOP/s); the other variants do not
+  // spill in their main loop and only lose by the extra VALU work. The non-causal
+  // d = 128 variant recomputes them in its masked tiles (the ragged last tile) only,
+  // where the mask's registers made it spill (N = 1000, B = 8, H = 32: 683 -> 825).
+  constexpr bool RECOMPUTE_OFFSETS = D == 128 && CAUSAL;
   constexpr bool RECOMPUTE_MASKED = RECOMPUTE_OFFSETS || (D == 128 && !CAUSAL && BN == 64);
   int koff_live[D / 16], voff_live[D / 32][2];
   frag_offsets(lane, koff_live, voff_live);
@@ -549,69 +548,78 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   write_rows<D, BF16, QB>(p, sl, bh, wi.split, wq0, lane, acc_o, ref, l_run);
 }
 
+// Scheduling groups for one pipelined tile: NMF MFMAs, in chunks of QKT products
+// S = K Q^T (one ds_read_b128 each) followed by PVT products U += V^T P^T (two
+// transposing reads each). The LDS reads of MFMA i + PREF are issued after MFMA i,
+// and VPM VALU instructions follow every MFMA.
+template <int I, int NMF, int QKT, int PVT, int PREF, int VPM>
+struct Interleave {
+  static constexpr int reads(int i) { return (i % (QKT + PVT)) < QKT ? 1 : 2; }
+  static constexpr int first() {
+    int n = 0;
+    for (int i = 0; i < PREF && i < NMF; ++i) n += reads(i);
+    return n;
+  }
+  static __device__ __forceinline__ void emit() {
+    if constexpr (I == 0) __builtin_amdgcn_sched_group_barrier(0x100, first(), 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);                              // VALU
+    if constexpr (I + PREF < NMF) __builtin_amdgcn_sched_group_barrier(0x100, reads(I + PREF), 0);
+    if constexpr (I + 1 < NMF) Interleave<I + 1, NMF, QKT, PVT, PREF, VPM>::emit();
+  }
+};
+
 // ------------------------------------------------------------------------------------
-// Ping-pong kernel: eight waves, two per SIMD, taking turns on the matrix pipe.
+// Software-pipelined four-wave kernel
 // ------------------------------------------------------------------------------------
 //
-// A wave cannot overlap its own MFMAs with its own VALU work: measured on gfx950, one
-// wave interleaving an MFMA with 16 FMAs takes about as long as the two streams
-// back to back, while an MFMA-only wave and a VALU-only wave sharing a SIMD run at
-// nearly their standalone rates. So the workgroup has eight waves; waves w and w+4
-// share a SIMD (measured with HW_ID), and the two groups G0 = {0..3}, G1 = {4..7}
-// run the same sequence of clusters one phase apart, separated by workgroup barriers:
+// On gfx950 one wave issues a VALU instruction only every ~6 cycles while the SIMD's
+// VALU pipe accepts one every ~4 (v_exp_f32 holds it ~8.7 cycles), and a wave's
+// MFMAs run on the matrix pipe while the same wave keeps issuing independent VALU
+// instructions (measured with a probe of issue rates). So each wave interleaves, in
+// one instruction stream, the softmax of tile j with the two products that do not
+// depend on it: S(j+1) = K(j+1) Q^T and U += V(j-1)^T P(j-1)^T. Every tile of a wave
+// is then one mixed stream of 16 (d = 64) or 32 (d = 128) MFMAs and ~113 VALU
+// instructions, and the two waves of a SIMD fill both pipes without having to run
+// in opposite phases.
 //
-//   phase 2j   : G0 runs M(j)            G1 runs V(j-1)
-//   phase 2j+1 : G0 runs V(j)            G1 runs M(j)
-//
-//   M(j) = S(j) = K(j) Q^T and U += V(j-1)^T P(j-1)^T    (16 MFMAs from registers)
-//   V(j) = softmax of S(j) into P(j); LDS reads of the K(j+1) and V(j) fragments
-//          that M(j+1) consumes                          (VALU and LDS)
-//
-// so on every SIMD one wave feeds the matrix pipe while the other does its softmax.
-// K and V tiles are double-buffered in LDS. The G0 waves issue all direct loads:
-// K(j+2) and V(j+1) at the end of V(j) (phase 2j+1), after their own reads of that
-// cluster, and wait for them at the end of M(j+1) (phase 2j+2), before the barrier.
-// K(j+1) and V(j) are read in phases 2j+1 (G0) and 2j+2 (G1); their stages are
-// refilled from the end of phase 2j+3 on. Every barrier also waits for the wave's
-// LDS reads, so no stage is overwritten while a read of it is in flight. No wave
-// ever reads LDS while one of its own direct loads is pending, so the compiler
-// needs no wait between the two even though it cannot tell the stages apart.
-template <int D, bool BF16, bool CAUSAL, int QB, int BN>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fa_fwd_pp_kernel(Params p) {
+// Iteration j (one barrier):
+//   wait for this wave's loads, barrier     K(j+1), V(j-1) are in LDS stage (j+1)%2
+//   start loads K(j+2), V(j) -> stage j%2   (their previous contents K(j), V(j-2) were
+//                                            last read in iteration j-1)
+//   softmax S(j) -> P(j)   interleaved with   S(j+1) = K(j+1) Q^T,  U += V(j-1)^T P(j-1)^T
+// A reference move (rare) scales U after U += V(j-1)^T P(j-1)^T, which precedes it in
+// program order, and before P(j) enters U one iteration later.
+template <int D, bool BF16, bool CAUSAL, int NW, int BN>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD))) void fa_fwd_pipe_kernel(Params p) {
 #pragma clang fp contract(off)
-  constexpr int NWAVES = 8;
-  constexpr int BM = 32 * NWAVES * QB;        // query rows per workgroup
-  constexpr int TILE = BN * D;                // elements per K or V tile
+  constexpr int BM = 32 * NW;
+  constexpr int TILE = BN * D;
   constexpr int DMA_PER_TILE = TILE * 2 / 1024;
-  constexpr int LOADS_PER_WAVE = 2 * DMA_PER_TILE / (NWAVES / 2);   // G0 issues all loads
+  constexpr int DMA_PER_WAVE = DMA_PER_TILE / NW;
   constexpr int ROWS_PER_DMA = 1024 / (2 * D);
   constexpr int PATS = 16 / ROWS_PER_DMA;
   constexpr int NKB = BN / 32, NKS = D / 16, NDB = D / 32, NTT = BN / 16;
-  constexpr int NQK = NKB * NKS * QB, NPV = NDB * NTT * QB;
+  constexpr int NQK = NKB * NKS, NPV = NDB * NTT;      // MFMAs of each product per tile
+  constexpr int QK_PER_TT = NQK / NTT, PV_PER_TT = NPV / NTT;
   static_assert(BN % 32 == 0 && (D == 64 || D == 128), "tile shape");
-  static_assert((2 * DMA_PER_TILE) % (NWAVES / 2) == 0, "every G0 wave issues the same number of loads");
-  static_assert(NQK == NPV, "the M cluster interleaves the two products one to one");
+  static_assert(DMA_PER_TILE % NW == 0, "every wave issues the same number of loads");
+  static_assert(NQK % NTT == 0 && NPV % NTT == 0, "products spread evenly over the softmax chunks");
   using f32x2 = float __attribute__((ext_vector_type(2)));
   using e16x2 = typename std::conditional<BF16, __bf16 __attribute__((ext_vector_type(2))),
                                           _Float16 __attribute__((ext_vector_type(2)))>::type;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-  // One LDS array holding the four stages: with the loop unrolled by two each stage
-  // is a compile-time offset that folds into the read instructions, so the fragment
-  // addresses need one register each, not one per stage. (One object is enough here:
-  // no wave reads LDS while one of its own direct loads is pending.)
-  __shared__ __attribute__((aligned(1024))) short lds[4 * TILE];
-  short* const lds_k0 = lds;
-  short* const lds_k1 = lds + TILE;
-  short* const lds_v0 = lds + 2 * TILE;
-  short* const lds_v1 = lds + 3 * TILE;
+  __shared__ __attribute__((aligned(1024))) short lds_k0[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_k1[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_v0[TILE];
+  __shared__ __attribute__((aligned(1024))) short lds_v1[TILE];
 
-  // ---- work item ----
   const WorkItem wi = work_item<CAUSAL>(p);
   const int bh = wi.bh;
-  const int Nq = p.Nq, Nk = p.Nk, off = p.causal_off;
+  const int Nk = p.Nk, off = p.causal_off;
   const int m0 = wi.mb * BM;
-  const int kb = wi.split * p.split_keys;      // keys [kb, ke) of this workgroup's range
+  const int kb = wi.split * p.split_keys;
   const int ke = min(Nk, kb + p.split_keys);
   const Slice sl = slice_of(p, bh);
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(sl.q, p.q_bytes);
@@ -620,299 +628,278 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2;                  // 0: leads by one phase, 1: follows
   const int lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
-  // The two waves of a SIMD (w, w+4) own adjacent row blocks, so under a causal
-  // mask they run out of work on the same tile.
-  const int wq0 = m0 + 32 * QB * (2 * (wave & 3) + grp);
+  const int wq0 = m0 + wave * 32;
   const float c = p.c;
 
-  // tiles the workgroup streams, tiles this wave computes, tiles it needs no mask
-  // for; tile j holds keys kb + j BN ...
-  // query indices of the rows, as in fa_fwd_kernel (packed query heads: any of 0 .. qmod - 1)
+  // LDS fragment offsets, as in fa_fwd_kernel
+  auto frag_offsets = [](int ln, int (&ko)[NKS], int (&vo)[NDB][2]) __attribute__((always_inline)) {
+    const int r32 = ln & 31, h = ln >> 5;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) ko[ks] = r32 * D + (((2 * ks + h) ^ swz<D>(r32)) << 3);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        const int r = 4 * h + ((ln & 15) >> 2) + 8 * sec;
+        const int ch = 4 * db + 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
+        vo[db][sec] = r * D + ((ch ^ swz<D>(r)) << 3) + 4 * (ln & 1);
+      }
+  };
+  // With every operand of a 64-key tile live at d = 128 the loop would spill; there
+  // the offsets are recomputed per tile from a copy of the lane index the compiler
+  // cannot hoist (248 registers, no spill).
+  constexpr bool RECOMP = D == 128 && BN == 64;
+  int koff[NKS], voff[NDB][2];
+  frag_offsets(lane, koff, voff);
+  uint32_t dma_off_k[PATS], dma_off_v[PATS];
+#pragma unroll
+  for (int q = 0; q < PATS; ++q) {
+    const int r_local = (16 * lane) / (2 * D);
+    const int pch = ((16 * lane) % (2 * D)) / 16;
+    const int r = ROWS_PER_DMA * ((q + wave) % PATS) + r_local;
+    const int col = (pch ^ swz<D>(r)) << 3;
+    dma_off_k[q] = (uint32_t)((r_local * p.k_sr + col) * 2);
+    dma_off_v[q] = (uint32_t)((r_local * p.v_sr + col) * 2);
+  }
+  auto issue_tile_load = [&](const __amdgpu_buffer_rsrc_t& rsrc, const uint32_t (&lane_off)[PATS], int sr,
+                             short* dst, int n0) {
+#pragma unroll
+    for (int kk = 0; kk < DMA_PER_WAVE; ++kk) {
+      const int i = kk * NW + wave;
+      buffer_load16_to_lds<0>(rsrc, dst + 512 * i, lane_off[(kk * NW) % PATS],
+                              (uint32_t)((n0 + ROWS_PER_DMA * i) * sr * 2));
+    }
+  };
+
+  i16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    qf[ks] = buffer_load16(rq, (uint32_t)(((wq0 + l32) * p.q_sr + ks * 16 + 8 * hi) * 2));
+  f32x16 acc_o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
+  float ref = -INFINITY, nb = 0.f, l_run = 0.f;
+
   const bool packed = p.qmod > 0;
   const int wg_last_q = packed ? p.qmod - 1 : m0 + BM - 1;
   const int w_first_q = packed ? 0 : wq0;
-  const int w_last_q = packed ? p.qmod - 1 : wq0 + 32 * QB - 1;
+  const int w_last_q = packed ? p.qmod - 1 : wq0 + 31;
   const int n_end = CAUSAL ? min(ke, wg_last_q + 1 + off) : ke;
-  const int T = n_end > kb ? (n_end - kb + BN - 1) / BN : 0;
-  int Tw = 0, n_full = 0;
-  if (wq0 < Nq) {
+  const int T = n_end > kb ? (n_end - kb + BN - 1) / BN : 0;          // tiles the workgroup streams
+  int Tw = 0, n_full = 0;                                               // tiles this wave computes / needs no mask for
+  if (wq0 < p.Nq) {
     const int w_end = CAUSAL ? min(ke, w_last_q + 1 + off) : ke;
     Tw = w_end > kb ? (w_end - kb + BN - 1) / BN : 0;
+    if (Tw > T) Tw = T;
     const int full_end = CAUSAL ? min(ke, w_first_q + 1 + off) : ke;
     n_full = min(Tw, full_end > kb ? (full_end - kb) / BN : 0);
   }
 
-  // ---- LDS fragment offsets (elements), as in fa_fwd_kernel ----
-  int koff[NKS];
+  // ---- the pieces of one iteration ----
+  // i-th MFMA of S = K Q^T (kb fastest, so that consecutive MFMAs are independent)
+  auto qk_mfma = [&](f32x16 (&s)[NKB], const short* kbuf, int i, const int (&ko)[NKS]) __attribute__((always_inline)) {
+    const int ks = i / NKB, kbk = i % NKB;
+    const i16x8 a = *(const i16x8*)(kbuf + kbk * 32 * D + ko[ks]);
+    s[kbk] = mfma_32x32x16<BF16>(a, qf[ks], ks == 0 ? f32x16{} : s[kbk]);
+  };
+  // i-th MFMA of U += V^T P^T (db fastest)
+  auto pv_mfma = [&](const i16x8 (&pw)[NTT], const short* vbuf, int i, const int (&vo)[NDB][2]) __attribute__((always_inline)) {
+    const int tt = i / NDB, db = i % NDB;
+    const short* src = vbuf + ((tt >> 1) * 32 + 16 * (tt & 1)) * D;
+    const i16x4 a0 = ds_read_tr16(src + vo[db][0]);
+    const i16x4 a1 = ds_read_tr16(src + vo[db][1]);
+    acc_o[db] = mfma_32x32x16<BF16>(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), pw[tt], acc_o[db]);
+  };
+  // weights of 16 keys (chunk tt) of s against the current reference, packed into pw[tt];
+  // adds them to the two partial sums
+  auto weights_chunk = [&](const f32x16 (&s)[NKB], i16x8 (&pw)[NTT], float (&part)[2], int tt) __attribute__((always_inline)) {
+    const int kbk = tt >> 1, base = 8 * (tt & 1);
+    float e[8];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) koff[ks] = l32 * D + (((2 * ks + hi) ^ swz<D>(l32)) << 3);
-  int voff[NDB][2];
+    for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kbk][base + i], c, nb));
+    e16x2 h[4];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
+    for (int i = 0; i < 4; ++i) h[i] = __builtin_convertvector((f32x2){e[2 * i], e[2 * i + 1]}, e16x2);
+    pw[tt] = __builtin_bit_cast(i16x8, ((u32x4){__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
+                                                 __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])}));
 #pragma unroll
-    for (int sec = 0; sec < 2; ++sec) {
-      const int r = 4 * hi + ((lane & 15) >> 2) + 8 * sec;
-      const int ch = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-      voff[db][sec] = r * D + ((ch ^ swz<D>(r)) << 3) + 4 * (lane & 1);
+    for (int i = 0; i < 8; ++i) part[i & 1] = (tt == 0 && i < 2) ? e[i] : part[i & 1] + e[i];
+  };
+  // hidden scores to -inf: key > min(Nk - 1, query + off), one compare per score
+  auto apply_mask = [&](f32x16 (&s)[NKB], int n0) __attribute__((always_inline)) {
+    int query = wq0 + l32;
+    if (CAUSAL && packed) query %= p.qmod;
+    const int lim = (CAUSAL ? min(Nk - 1, query + off) : Nk - 1) - (n0 + 4 * hi);
+#pragma unroll
+    for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (kbk * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kbk][r] = -INFINITY;
+  };
+  // After the weights of a tile: keep the reference while every lane's sum is at most
+  // kSumMax; else (or on a row's first tile) move it to the row maximum, rescale l and
+  // U (which already holds every earlier tile), and redo the weights.
+  auto finish_softmax = [&](const f32x16 (&s)[NKB], i16x8 (&pw)[NTT], float rs) __attribute__((always_inline)) {
+    if (__builtin_amdgcn_ballot_w64(!(rs <= kSumMax) || ref == -INFINITY)) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kbk = 0; kbk < NKB; ++kbk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kbk][r]);
+      const float cand = max_halves(mx) * c;
+      const float ref_new = cand > ref ? cand : ref;
+      const float alpha = (ref_new == ref) ? 1.f : __builtin_amdgcn_exp2f(ref - ref_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+      ref = ref_new;
+      nb = (ref_new == -INFINITY) ? 0.f : -ref_new;
+      float part[2];
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) weights_chunk(s, pw, part, tt);
+      rs = part[0] + part[1];
     }
+    l_run += rs;
+  };
 
-  // ---- direct-load assignment: load i of a phase (i < DMA_PER_TILE: K chunk i,
-  // else V chunk i - DMA_PER_TILE) is issued by G0 wave i % 4 ----
-  uint32_t dma_off[LOADS_PER_WAVE];
-  int dma_chunk[LOADS_PER_WAVE];
-  bool dma_is_k[LOADS_PER_WAVE];
-#pragma unroll
-  for (int t = 0; t < LOADS_PER_WAVE; ++t) {
-    const int i = (wave & 3) + (NWAVES / 2) * t;
-    dma_is_k[t] = i < DMA_PER_TILE;
-    const int ch = dma_is_k[t] ? i : i - DMA_PER_TILE;
-    dma_chunk[t] = ch;
-    const int r_local = (16 * lane) / (2 * D);
-    const int pch = ((16 * lane) % (2 * D)) / 16;
-    const int r = ROWS_PER_DMA * (ch % PATS) + r_local;
-    dma_off[t] = (uint32_t)((r_local * (dma_is_k[t] ? p.k_sr : p.v_sr) + ((pch ^ swz<D>(r)) << 3)) * 2);
-  }
-  // loads of K(jk) into kdst (if has_k) and V(jv) into vdst (if has_v); wave-uniform flags
-  auto issue_loads = [&](short* kdst, short* vdst, int jk, int jv, bool has_k, bool has_v) __attribute__((always_inline)) {
-#pragma unroll
-    for (int t = 0; t < LOADS_PER_WAVE; ++t) {
-      if (dma_is_k[t]) {
-        if (has_k)
-          buffer_load16_to_lds(rk, kdst + 512 * dma_chunk[t], dma_off[t],
-                               (uint32_t)((kb + jk * BN + ROWS_PER_DMA * dma_chunk[t]) * p.k_sr * 2));
-      } else {
-        if (has_v)
-          buffer_load16_to_lds(rv, vdst + 512 * dma_chunk[t], dma_off[t],
-                               (uint32_t)((kb + jv * BN + ROWS_PER_DMA * dma_chunk[t]) * p.v_sr * 2));
-      }
+  // Steady-state iteration: softmax of s_cur -> p_cur, interleaved with
+  // s_next = K(j+1) Q^T and U += V(j-1)^T p_prev^T.
+  auto body = [&](f32x16 (&s_cur)[NKB], f32x16 (&s_next)[NKB], i16x8 (&p_cur)[NTT], const i16x8 (&p_prev)[NTT],
+                  const short* kbuf, const short* vbuf, int n0, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    int ko_f[NKS], vo_f[NDB][2];
+    if constexpr (RECOMP) {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      frag_offsets(ln, ko_f, vo_f);
     }
-  };
-  // End of a phase: wait for this wave's LDS reads (always) and direct loads (if
-  // wait_loads), then the workgroup barrier. No instruction moves across it.
-  auto phase_end = [&](bool wait_loads) __attribute__((always_inline)) {
-    if (wait_loads) __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-    else __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0)
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // ---- registers ----
-  i16x8 qf[QB][NKS];                 // Q^T, B operand of S^T = K Q^T
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[qb][ks] = buffer_load16(rq, (uint32_t)(((wq0 + 32 * qb + l32) * p.q_sr + ks * 16 + 8 * hi) * 2));
-  f32x16 acc_o[QB][NDB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[qb][db][r] = 0.f;
-  float ref[QB], nb[QB], l_run[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { ref[qb] = -INFINITY; nb[qb] = 0.f; l_run[qb] = 0.f; }
-  i16x8 kf[NKB][NKS];                // K fragments of the tile the next M cluster multiplies
-  i16x8 vf[NDB][NTT];                // V^T fragments of the tile whose P is pending
-  f32x16 s[QB][NKB];                 // scores, then weights, of the current tile
-  i16x8 pk[QB][NTT];                 // pending P as 16-bit B operands
-
-  auto read_k = [&](const short* kbuf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) kf[kb][ks] = *(const i16x8*)(kbuf + kb * 32 * D + koff[ks]);
-  };
-  auto read_v = [&](const short* vbuf) __attribute__((always_inline)) {
+    const int(&ko)[NKS] = RECOMP ? ko_f : koff;
+    const int(&vo)[NDB][2] = RECOMP ? vo_f : voff;
+    if constexpr (MASK) apply_mask(s_cur, n0);
+    float part[2];
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
-      const short* src = vbuf + ((tt >> 1) * 32 + 16 * (tt & 1)) * D;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const i16x4 a0 = ds_read_tr16(src + voff[db][0]);
-        const i16x4 a1 = ds_read_tr16(src + voff[db][1]);
-        vf[db][tt] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+      for (int m = 0; m < QK_PER_TT; ++m) qk_mfma(s_next, kbuf, tt * QK_PER_TT + m, ko);
+#pragma unroll
+      for (int m = 0; m < PV_PER_TT; ++m) pv_mfma(p_prev, vbuf, tt * PV_PER_TT + m, vo);
+      weights_chunk(s_cur, p_cur, part, tt);
     }
-  };
-  // i-th MFMA of each product: QK steps run ks-major so that consecutive steps of one
-  // accumulator are NQK / NKS apart; PV steps run tt-major likewise.
-  auto qk_step = [&](int i) __attribute__((always_inline)) {
-    const int ks = i / (NKB * QB), kb = (i / QB) % NKB, qb = i % QB;
-    if (ks == 0) s[qb][kb] = mfma_32x32x16<BF16>(kf[kb][ks], qf[qb][ks], (f32x16){});
-    else s[qb][kb] = mfma_32x32x16<BF16>(kf[kb][ks], qf[qb][ks], s[qb][kb]);
-  };
-  auto pv_step = [&](int i) __attribute__((always_inline)) {
-    const int tt = i / (NDB * QB), db = (i / QB) % NDB, qb = i % QB;
-    acc_o[qb][db] = mfma_32x32x16<BF16>(vf[db][tt], pk[qb][tt], acc_o[qb][db]);
-  };
-  // M cluster: both products, interleaved one to one. It runs in every iteration of
-  // every wave, so that the loop has one code path: where a product is not needed
-  // its result is unused (S of a tile past this wave's rows) or zero (P is zero
-  // before the first tile and after the wave's last one).
-  auto m_cluster = [&]() __attribute__((always_inline)) {
+    // Instruction order: the LDS reads run three MFMAs ahead of the MFMA that consumes
+    // them; every MFMA is followed by an equal share of the softmax's VALU work (28
+    // instructions per 16 keys: FMA, exp and add per weight, one pack per two).
+    Interleave<0, NQK + NPV, QK_PER_TT, PV_PER_TT, 3, (28 * NTT) / (NQK + NPV)>::emit();
+    // the packed weights are formed before the reference check (a redo rewrites them),
+    // so that the packing joins the interleaved stream instead of trailing it
 #pragma unroll
-    for (int i = 0; i < NQK; ++i) { qk_step(i); pv_step(i); }
+    for (int tt = 0; tt < NTT; ++tt) asm volatile("" ::"v"(p_cur[tt]));
+    finish_softmax(s_cur, p_cur, part[0] + part[1]);
   };
 
-  // Softmax of tile j (keys n0..n0+BN) in s, into pk; l, ref and (rarely) U updated.
-  // The common path needs no row maximum: the weights are formed against the current
-  // reference, P = 2^(c x + nb) with nb = -ref, and their per-lane sum both updates l
-  // and checks the reference. While every lane's sum of this tile's weights is at
-  // most kSumMax, every weight is too (and far inside fp16's range). Otherwise (a new
-  // maximum well above the reference, an infinite weight, or the first tile, whose
-  // reference is still -inf) the wave takes the rare path: each query's reference
-  // moves up to its row maximum, l and U are scaled by alpha = 2^(ref_old - ref_new),
-  // and the tile's weights are recomputed (s is still intact). After a move every
-  // weight of the tile is at most 1, so one redo suffices.
-  auto weights = [&](float (&rs)[QB]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float part[2];   // two partial sums: shorter dependency chains
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
-        const int kb = tt >> 1, base = 8 * (tt & 1);
-        float e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][base + i], c, nb[qb]));
-        e16x2 h[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = __builtin_convertvector((f32x2){e[2 * i], e[2 * i + 1]}, e16x2);
-        pk[qb][tt] = __builtin_bit_cast(i16x8, ((u32x4){__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]),
-                                                        __builtin_bit_cast(uint32_t, h[2]), __builtin_bit_cast(uint32_t, h[3])}));
-        // l sums the fp32 weights. (A dot2 over the packed weights would issue half as
-        // many instructions, but on gfx950 it waits for the matrix pipe, which the
-        // other wave of the SIMD keeps busy: measured 24 cycles per dot2 against 6 per add.)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) part[i & 1] = (tt == 0 && i < 2) ? e[i] : part[i & 1] + e[i];
-      }
-      rs[qb] = part[0] + part[1];
-    }
-  };
-  auto softmax = [&](int n0, bool mask) __attribute__((always_inline)) {
-    if (mask) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        int query = wq0 + 32 * qb + l32;
-        if (CAUSAL && packed) query %= p.qmod;
-        // hidden: key > min(Nk - 1, query + off), as in the four-wave kernel
-        const int lim = (CAUSAL ? min(Nk - 1, query + off) : Nk - 1) - (n0 + 4 * hi);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[qb][kb][r] = -INFINITY;
-      }
-    }
-    float rs[QB];
-    weights(rs);
-    bool redo = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) redo |= !(rs[qb] <= kSumMax) || ref[qb] == -INFINITY;
-    if (__builtin_amdgcn_ballot_w64(redo)) {   // wave-uniform, rare after the first tile
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-        const float cand = max_halves(mx) * c;             // fl(c * row max), -inf if none valid
-        const float ref_new = cand > ref[qb] ? cand : ref[qb];
-        // 1 if the reference did not move (also while it is still -inf: a row with no
-        // visible key so far), 0 when it leaves -inf
-        const float alpha = (ref_new == ref[qb]) ? 1.f : __builtin_amdgcn_exp2f(ref[qb] - ref_new);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[qb][db][r] *= alpha;
-        ref[qb] = ref_new;
-        nb[qb] = (ref_new == -INFINITY) ? 0.f : -ref_new;  // -inf guard: base 0 until a valid key
-      }
-      weights(rs);
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+  auto sync_tile = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
   };
 
-  // The compiler may move arithmetic across the barrier asm (it is not a memory
-  // operation); an empty asm that reads and writes a value pins its computation to
-  // the phase that produced it.
-  auto pin_softmax_state = [&]() __attribute__((always_inline)) {
+  f32x16 s_a[NKB], s_b[NKB];
+  i16x8 p_a[NTT], p_b[NTT];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) asm volatile("" : "+v"(pk[qb][tt]));
-      asm volatile("" : "+v"(l_run[qb]), "+v"(ref[qb]), "+v"(nb[qb]));
-    }
-  };
-  // V cluster of tile j: fragment reads for the next M cluster (always issued; a
-  // stage holding no needed tile is read harmlessly), then the softmax, or P = 0
-  // for a tile this wave does not compute.
-  auto v_cluster = [&](int j, const short* k_next, const short* v_cur) __attribute__((always_inline)) {
-    read_k(k_next);
-    read_v(v_cur);
-    if (j < Tw) {
-      softmax(kb + j * BN, j >= n_full);
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) pk[qb][tt] = (i16x8){};
-    }
-    pin_softmax_state();
-  };
+  for (int tt = 0; tt < NTT; ++tt) { p_a[tt] = (i16x8){}; p_b[tt] = (i16x8){}; }
 
-  // ---- prologue: K(0), V(0), K(1) in LDS; K(0) fragments in registers ----
+  // ---- prologue: K(0) -> stage 0; S(0). V stage 1 is zeroed: the first main
+  // iteration multiplies it by P(-1) = 0, and LDS may hold NaN patterns. ----
+  if (T > 0) issue_tile_load(rk, dma_off_k, p.k_sr, lds_k0, kb);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int i = tid * 8; i < TILE; i += NW * 64 * 8) *(i16x8*)(lds_v1 + i) = (i16x8){};
+  sync_tile();
+  if (T > 1) issue_tile_load(rk, dma_off_k, p.k_sr, lds_k1, kb + BN);
+  if (Tw > 0) {
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) pk[qb][tt] = (i16x8){};
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) vf[db][tt] = (i16x8){};
-  if (grp == 0) {
-    issue_loads(lds_k0, lds_v0, 0, 0, true, true);
-    if (T > 1) issue_loads(lds_k1, lds_v1, 1, 0, true, false);
+    for (int i = 0; i < NQK; ++i) qk_mfma(s_a, lds_k0, i, koff);
   }
-  phase_end(true);
-  read_k(lds_k0);
-  if (grp == 1) phase_end(false);            // G1 sits out phase 0
 
-  // iteration j: M(j), barrier, V(j), barrier. Unrolled by two, so that every LDS
-  // stage is named at compile time and its offset folds into the instructions.
-  auto iteration = [&](int j, auto odd_tag) __attribute__((always_inline)) {
+  // ---- main loop: iterations j < n_main need no mask, and S(j+1) and P(j-1) are both
+  // needed (P(-1) = 0 enters U harmlessly) ----
+  const int n_main = min(n_full, Tw - 1);
+  // iteration j reads K(j+1) and V(j-1) from stage (j+1)%2; loads K(j+2), V(j) into stage j%2
+  auto main_iter = [&](int j, auto odd_tag) __attribute__((always_inline)) {
     constexpr bool ODD = decltype(odd_tag)::value;
-    short* k_ld = ODD ? lds_k1 : lds_k0;          // K(j+2) -> stage j%2
-    short* v_ld = ODD ? lds_v0 : lds_v1;          // V(j+1) -> stage (j+1)%2
-    const short* k_rd = ODD ? lds_k0 : lds_k1;    // K(j+1) in stage (j+1)%2
-    const short* v_rd = ODD ? lds_v1 : lds_v0;    // V(j) in stage j%2
-    m_cluster();
-    phase_end(grp == 0);
-    v_cluster(j, k_rd, v_rd);
-    if (grp == 0) issue_loads(k_ld, v_ld, j + 2, j + 1, j + 2 < T, j + 1 < T);
-    phase_end(false);
+    short* k_rd = ODD ? lds_k0 : lds_k1;
+    short* v_rd = ODD ? lds_v0 : lds_v1;
+    short* k_wr = ODD ? lds_k1 : lds_k0;
+    short* v_wr = ODD ? lds_v1 : lds_v0;
+    const int n0 = kb + j * BN;
+    sync_tile();
+    if (j + 2 < T) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + 2 * BN);
+    issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
+    if constexpr (ODD) body(s_b, s_a, p_b, p_a, k_rd, v_rd, n0, std::false_type{});
+    else body(s_a, s_b, p_a, p_b, k_rd, v_rd, n0, std::false_type{});
   };
   int j = 0;
-  for (; j + 1 < T; j += 2) {
-    iteration(j, std::false_type{});
-    iteration(j + 1, std::true_type{});
+  for (; j + 1 < n_main; j += 2) {
+    main_iter(j, std::false_type{});
+    main_iter(j + 1, std::true_type{});
   }
-  if (j < T) iteration(j, std::false_type{});
-
-  // ---- final cluster: the last pending P V, then O = U / l and LSE ----
-  // (its P is zero unless this wave computed the last tile)
+  // ---- tail: the rest of the tiles, one at a time, with the register sets swapped
+  // to the even/odd naming by a copy when needed ----
+  if (j < n_main) {
+    // after an even iteration S(j+1) is in s_b and P(j) in p_a
+    main_iter(j, std::false_type{});
+    ++j;
 #pragma unroll
-  for (int i = 0; i < NPV; ++i) pv_step(i);
-  write_rows<D, BF16, QB>(p, sl, bh, wi.split, wq0, lane, acc_o, ref, l_run);
-  if (grp == 0) phase_end(false);            // G0 matches G1's barrier count
+    for (int kbk = 0; kbk < NKB; ++kbk) s_a[kbk] = s_b[kbk];
+  } else if (j > 0) {
+    // after an odd iteration S(j+1) is in s_a and P(j) in p_b
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) p_a[tt] = p_b[tt];
+  }
+  bool have_prev = j > 0;    // p_a holds P(j-1)
+  for (; j < T; ++j) {
+    short* k_rd = (j & 1) ? lds_k0 : lds_k1;
+    short* v_rd = (j & 1) ? lds_v0 : lds_v1;
+    short* k_wr = (j & 1) ? lds_k1 : lds_k0;
+    short* v_wr = (j & 1) ? lds_v1 : lds_v0;
+    const int n0 = kb + j * BN;
+    sync_tile();
+    if (j + 2 < T) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + 2 * BN);
+    issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
+    // S(j) is in s_a, P(j-1) in p_a
+    if (j + 1 < Tw) {
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) qk_mfma(s_b, k_rd, i, koff);
+    }
+    if (have_prev) {
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) pv_mfma(p_a, v_rd, i, voff);
+    }
+    have_prev = j < Tw;
+    if (have_prev) {
+      if (j >= n_full) apply_mask(s_a, n0);
+      float part[2];
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) weights_chunk(s_a, p_a, part, tt);
+      finish_softmax(s_a, p_a, part[0] + part[1]);
+    }
+#pragma unroll
+    for (int kbk = 0; kbk < NKB; ++kbk) s_a[kbk] = s_b[kbk];
+  }
+  sync_tile();                                   // V(T-1) is in LDS stage (T-1)%2
+  if (have_prev) {
+    const short* v_rd = ((T - 1) & 1) ? lds_v1 : lds_v0;
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) pv_mfma(p_a, v_rd, i, voff);
+  }
+  float ref_a[1] = {ref}, l_a[1] = {l_run};
+  f32x16 acc_w[1][NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc_w[0][db] = acc_o[db];
+  write_rows<D, BF16, 1>(p, sl, bh, wi.split, wq0, lane, acc_w, ref_a, l_a);
 }
 
 // ------------------------------------------------------------------------------------
@@ -1016,14 +1003,15 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
 // Host side
 // ------------------------------------------------------------------------------------
 
-// Compiled tile shapes: block_m query rows per workgroup (NW waves x QB blocks of
-// 32 queries per wave) and block_n keys per K/V tile.
-struct TileShape { int bm, bn, nw, qb; bool d128; };
+// Compiled tile shapes: block_m query rows per workgroup (NW waves, each owning 32
+// query rows) and block_n keys per K/V tile, and the head sizes each is built for.
+// fa_fwd_kernel runs (64, 64), (128, 64) and (128, 32) at d = 64; fa_fwd_pipe_kernel
+// runs (128, 32) at d = 128 and the eight-wave tiles (256, 32 at d = 128 only: a
+// d = 64 tile of 32 keys is four 1 KB loads, fewer than the eight waves).
+struct TileShape { int bm, bn, nw; bool d64, d128; };
 constexpr TileShape kTiles[] = {
-    // fa_fwd_kernel: 2 or 4 waves, each owning 32 query rows
-    {64, 64, 2, 1, true}, {128, 64, 4, 1, true}, {128, 32, 4, 1, true},
-    // fa_fwd_pp_kernel: 8 waves in two groups taking turns on each SIMD's matrix pipe
-    {256, 32, 8, 1, true}, {256, 64, 8, 1, false}, {512, 32, 8, 2, false}};
+    {64, 64, 2, true, true}, {128, 64, 4, true, true}, {128, 32, 4, true, true},
+    {256, 32, 8, false, true}, {256, 64, 8, true, true}};
 
 template <int D, bool BF16>
 hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
@@ -1037,29 +1025,30 @@ hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool BF16, bool CAUSAL, int NW, int QB, int BN>
-hipError_t launch_one(const Params& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, NW, QB, BN>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
+template <int D, bool BF16, bool CAUSAL, int NW, int BN>
+hipError_t launch_four_wave(const Params& p, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, NW, 1, BN>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool BF16, bool CAUSAL, int QB, int BN>
-hipError_t launch_pp(const Params& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_pp_kernel<D, BF16, CAUSAL, QB, BN>), dim3(p.total_wgs), dim3(512), 0, stream, p);
+template <int D, bool BF16, bool CAUSAL, int NW, int BN>
+hipError_t launch_pipelined(const Params& p, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_fwd_pipe_kernel<D, BF16, CAUSAL, NW, BN>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
+// The launch for a tile of kTiles (tile_ok has accepted it for this D).
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_tile(const Params& p, int bm, int bn, hipStream_t stream) {
-  if (bm == 64 && bn == 64) return launch_one<D, BF16, CAUSAL, 2, 1, 64>(p, stream);
-  if (bm == 128 && bn == 64) return launch_one<D, BF16, CAUSAL, 4, 1, 64>(p, stream);
-  if (bm == 128 && bn == 32) return launch_one<D, BF16, CAUSAL, 4, 1, 32>(p, stream);
-  if (bm == 256 && bn == 32) return launch_pp<D, BF16, CAUSAL, 1, 32>(p, stream);
-  if constexpr (D == 64) {
-    // at d = 128 these fragments and accumulators do not fit 256 registers
-    if (bm == 256 && bn == 64) return launch_pp<D, BF16, CAUSAL, 1, 64>(p, stream);
-    if (bm == 512 && bn == 32) return launch_pp<D, BF16, CAUSAL, 2, 32>(p, stream);
+  if (bm == 64 && bn == 64) return launch_four_wave<D, BF16, CAUSAL, 2, 64>(p, stream);
+  if (bm == 128 && bn == 64) return launch_four_wave<D, BF16, CAUSAL, 4, 64>(p, stream);
+  if (bm == 128 && bn == 32) {
+    if constexpr (D == 64) return launch_four_wave<D, BF16, CAUSAL, 4, 32>(p, stream);
+    else return launch_pipelined<D, BF16, CAUSAL, 4, 32>(p, stream);
   }
+  if constexpr (D == 128)
+    if (bm == 256 && bn == 32) return launch_pipelined<D, BF16, CAUSAL, 8, 32>(p, stream);
+  if (bm == 256 && bn == 64) return launch_pipelined<D, BF16, CAUSAL, 8, 64>(p, stream);
   return hipErrorInvalidValue;
 }
 
@@ -1072,7 +1061,7 @@ hipError_t launch_d(const Params& p, bool bf16, bool causal, int bm, int bn, hip
 bool tile_ok(int64_t d, int bm, int bn) {
   if (d != 64 && d != 128) return false;
   for (const TileShape& t : kTiles)
-    if (t.bm == bm && t.bn == bn) return d == 64 || t.d128;
+    if (t.bm == bm && t.bn == bn) return d == 64 ? t.d64 : t.d128;
   return false;
 }
 
@@ -1100,18 +1089,24 @@ fa_status read_strides(const int64_t* st, int64_t H, int64_t N, int64_t d, int64
 void default_tile(int64_t N, int64_t d, int causal, int* bm, int* bn) {
   // Measured on MI355X (interleaved tile sweeps per workload family):
   //  - short sequences: the smallest tile, so that more workgroups exist;
-  //  - the four-wave kernel with one 32-query block per wave otherwise (causal row
-  //    blocks of uneven length balance better with small blocks): 64-key tiles
-  //    for long non-causal sequences (d = 64 and d = 128) and for causal d = 64
-  //    from N = 2048 (+10% at N = 2048, +17% at 8192), 32-key tiles otherwise.
-  //    At d = 128 the non-causal 64-key tile beats the eight-wave kernel
-  //    (1252 against 1191 TFLOP/s at N = 16384, 1143 against 990 at N = 4096).
+  //  - d = 64: the four-wave kernel (one 32-query block per wave; causal row blocks of
+  //    uneven length balance better with small blocks): 64-key tiles for long
+  //    non-causal sequences and for causal ones from N = 2048 (+10% at N = 2048,
+  //    +17% at 8192), 32-key tiles otherwise; the pipelined kernel measured 3% slower
+  //    at N = 4096 (the softmax's VALU work, not the overlap, sets the pace there);
+  //  - d = 128: the pipelined kernel with 32-key tiles, four waves under a causal mask
+  //    (+1.7% at N = 2048 against the four-wave kernel) and eight waves for long
+  //    non-causal sequences (+1.7% to +2.3% at N = 16384: one workgroup of 256 rows per
+  //    CU streams each K/V tile once for twice the rows); (128, 64) in between.
   if (N <= 128) {
     *bm = 64;
     *bn = 64;
+  } else if (d == 128) {
+    *bm = (!causal && N >= 4096) ? 256 : 128;
+    *bn = (!causal && N < 4096 && N > 256) ? 64 : 32;
   } else {
     *bm = 128;
-    *bn = ((!causal && N > 256) || (causal && d == 64 && N > 1024)) ? 64 : 32;
+    *bn = ((!causal && N > 256) || (causal && N > 1024)) ? 64 : 32;
   }
 }
 
@@ -1120,7 +1115,7 @@ void default_tile(int64_t N, int64_t d, int causal, int* bm, int* bn) {
 // lane): the four-wave tiles run one wave per SIMD per workgroup, two workgroups
 // per CU at 160..256 registers and three for the 32-key tiles at d = 64 (147..160);
 // the 2-wave (64, 64) tile fits two waves per SIMD at d = 64 (4 per CU) but needs
-// more than 256 registers at d = 128 (2 per CU); the eight-wave tiles fill a CU.
+// more than 256 registers at d = 128 (2 per CU); an eight-wave workgroup fills a CU.
 int wgs_per_cu(int bm, int bn, int64_t d) {
   if (bm == 64) return d == 64 ? 4 : 2;
   if (bm == 128) return (d == 64 && bn == 32) ? 3 : 2;
