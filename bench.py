@@ -79,7 +79,7 @@ def _pmc_rows(d, counter):
             if row["Counter_Name"] != counter:
                 continue
             name = row["Kernel_Name"]
-            if "fa_fwd_kernel" in name or "fa_fwd_pp_kernel" in name:
+            if "fa_fwd_kernel" in name or "fa_fwd_pipe_kernel" in name:
                 fa_vals.append((name, float(row["Counter_Value"])))
             elif "copyBuffer" in name:
                 copy_vals.append(float(row["Counter_Value"]))
