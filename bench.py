@@ -41,6 +41,9 @@ def parse():
                     help="counter-collection mode: a few launches of --workload, then a plain "
                          "device copy of COPY_BYTES (read and written once) to calibrate the "
                          "HBM byte counters; prints one JSON line")
+    ap.add_argument("--backward", action="store_true",
+                    help="with --profile: launch fa_bwd (after one fa_fwd for O and LSE) "
+                         "instead of fa_fwd")
     return ap.parse_args()
 
 
@@ -119,7 +122,7 @@ def stored_traffic(w):
     return rec
 
 
-def profile_mode(w, launches=3):
+def profile_mode(w, launches=3, backward=False):
     import torch
     import exact_attention_forward_fwd_amd as fa
     from exact_attention_forward_fwd_amd.workloads import make_inputs
@@ -130,15 +133,22 @@ def profile_mode(w, launches=3):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     tile = w.tile or (None, None)
-    for _ in range(launches):
+    for _ in range(1 if backward else launches):
         fa.fwd(q, k, v, scale=w.scale, causal=w.causal, block_m=tile[0], block_n=tile[1], out=o, lse=lse)
+    if backward:
+        # dO as in the bench's backward timing
+        g = torch.Generator("cpu").manual_seed(5000 + w.index)
+        do = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
+        for _ in range(launches):
+            fa.bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal)
     torch.cuda.synchronize()
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(launches):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"profile": w.name, "launches": launches, "copy_bytes": COPY_BYTES}), flush=True)
+    print(json.dumps({"profile": w.name, "backward": backward, "launches": launches, "copy_bytes": COPY_BYTES}),
+          flush=True)
 
 
 def time_calls(call, stream, steps):
@@ -375,7 +385,7 @@ def main():
     fa.load_library()
     w = WORKLOADS[args.workload]
     if args.profile:
-        profile_mode(w)
+        profile_mode(w, backward=args.backward)
         return
     r = time_workload(w, args.steps, args.warmup)
     tflops = w.flops / (r["ms_per_step"] * 1e-3) / 1e12
