@@ -208,7 +208,9 @@ def time_workload(w, steps, warmup):
 
 def time_split(w, steps, warmup):
     """Per-call device time of fa_fwd_split (attention launch + merge launch) at the
-    library's suggested split count, and of the unsplit fa_fwd_ex, on the same inputs."""
+    library's suggested split count, and of the unsplit call, on the same inputs: five
+    alternating rounds of steps / 5 back-to-back calls each; call_ms_median is the
+    median round."""
     import torch
     import exact_attention_forward_fwd_amd as fa
     from exact_attention_forward_fwd_amd.workloads import make_general_inputs
@@ -228,18 +230,26 @@ def time_split(w, steps, warmup):
     base = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), w.B, w.Hq, w.Hk, w.Nq, w.Nk,
             w.d, *st, float(w.scale), int(w.causal), dt, sp, 0, 0)
 
-    def run(n_splits):
+    def caller(n_splits):
         def call():
             rc = lib.fa_fwd_split(*base, n_splits, ws.data_ptr(), ws.numel())
             if rc != 0:
                 raise fa.FaError(rc, "fa_fwd_split")
-        for _ in range(warmup):
-            call()
-        t = time_calls(call, stream, steps)
-        return t["avg"], t["median"]
+        return call
 
-    avg, med = run(splits)
-    avg1, _ = run(1)
+    # the split and unsplit calls alternate in rounds, so that both see the same clock
+    call_s, call_1 = caller(splits), caller(1)
+    for _ in range(warmup):
+        call_s()
+        call_1()
+    rounds = 5
+    per = max(1, steps // rounds)
+    t_s, t_1 = [], []
+    for _ in range(rounds):
+        t_s.append(time_calls(call_s, stream, per)["avg"])
+        t_1.append(time_calls(call_1, stream, per)["avg"])
+    avg, avg1 = sum(t_s) / rounds, sum(t_1) / rounds
+    med = sorted(t_s)[rounds // 2]
     rec = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hk": w.Hk, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
            "dtype": w.dtype, "causal": w.causal, "splits": splits,
            "call_ms_avg": round(avg, 5), "call_ms_median": round(med, 5),

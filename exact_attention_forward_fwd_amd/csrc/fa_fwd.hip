@@ -1086,7 +1086,7 @@ fa_status read_strides(const int64_t* st, int64_t H, int64_t N, int64_t d, int64
   return FA_OK;
 }
 
-void default_tile(int64_t N, int64_t d, int causal, int* bm, int* bn) {
+void default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int* bm, int* bn) {
   // Measured on MI355X (interleaved tile sweeps per workload family):
   //  - short sequences: the smallest tile, so that more workgroups exist;
   //  - d = 64: the four-wave kernel (one 32-query block per wave; causal row blocks of
@@ -1096,13 +1096,22 @@ void default_tile(int64_t N, int64_t d, int causal, int* bm, int* bn) {
   //    at N = 4096 (the softmax's VALU work, not the overlap, sets the pace there);
   //  - d = 128: the pipelined kernel with 32-key tiles, four waves under a causal mask
   //    (+1.7% at N = 2048 against the four-wave kernel) and eight waves for long
-  //    non-causal sequences (+1.7% to +2.3% at N = 16384: one workgroup of 256 rows per
-  //    CU streams each K/V tile once for twice the rows); (128, 64) in between.
+  //    sequences (+1.7% to +2.3% at N = 16384 without a mask, +1.5% to +3.2% at
+  //    N = 4096 to 16384 with one: one workgroup of 256 rows per CU streams each K/V
+  //    tile once for twice the rows), provided the 256-row grid covers the 256 CUs
+  //    (without a mask) or twice that (with one, whose row blocks differ in length):
+  //    below that the 128-row tile was 19% to 35% faster (N = 4096 and 8192, 8 heads);
+  //    (128, 64) in between.
   if (N <= 128) {
     *bm = 64;
     *bn = 64;
   } else if (d == 128) {
-    *bm = (!causal && N >= 4096) ? 256 : 128;
+    // B H ceil(N / 256) >= need, without forming a product that could overflow
+    const int64_t need = causal ? 512 : 256;
+    const int64_t slices = (B >= need || H >= need) ? need : (B > 0 && H > 0 ? B * H : 0);
+    const int64_t per = N / 256 + (N % 256 != 0);      // 256-row blocks per slice
+    const bool eight = N >= 4096 && slices > 0 && (per >= need || slices >= (need + per - 1) / per);
+    *bm = eight ? 256 : 128;
     *bn = (!causal && N < 4096 && N > 256) ? 64 : 32;
   } else {
     *bm = 128;
@@ -1226,7 +1235,7 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
     Hq = Hk;
     group = 1;
   }
-  if (auto_tile) default_tile(Nq, d, causal, &bm, &bn);
+  if (auto_tile) default_tile(B, Hq, Nq, d, causal, &bm, &bn);
   if (!rows_fit(Nq, qs[2]) || !rows_fit(Nq, os[2]) || !rows_fit(Nk, ks[2]) || !rows_fit(Nk, vs[2]))
     return FA_ERR_TOO_LARGE;
   if (B >= ((int64_t)1 << 31) || Hq >= ((int64_t)1 << 31)) return FA_ERR_TOO_LARGE;
@@ -1315,7 +1324,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int64_t H, int64_t N, int64_t d, float scale, int causal, fa_dtype dtype,
                  hipStream_t stream) {
   int bm, bn;
-  default_tile(N, d, causal, &bm, &bn);
+  default_tile(B, H, N, d, causal, &bm, &bn);
   return run(q, k, v, o, lse, B, H, H, N, N, d, nullptr, nullptr, nullptr, nullptr, scale, causal, dtype,
              stream, bm, bn);
 }
@@ -1374,7 +1383,7 @@ int fa_split_default(int64_t B, int64_t Hq, int64_t Hk, int64_t Nq, int64_t Nk, 
     Nq *= Hq / Hk;
     Hq = Hk;
   }
-  if (block_m == 0 && block_n == 0) default_tile(Nq, d, causal, &block_m, &block_n);
+  if (block_m == 0 && block_n == 0) default_tile(B, Hq, Nq, d, causal, &block_m, &block_n);
   if (!tile_ok(d, block_m, block_n)) return 1;
   return split_heuristic(B, Hq, Nq, Nk, d, block_m, block_n);
 }
@@ -1383,10 +1392,9 @@ int fa_tile_supported(int64_t d, int block_m, int block_n) { return tile_ok(d, b
 
 fa_status fa_default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int* block_m,
                           int* block_n) {
-  (void)B; (void)H;
   if (!block_m || !block_n) return FA_ERR_NULL_PTR;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEADDIM;
-  default_tile(N, d, causal, block_m, block_n);
+  default_tile(B, H, N, d, causal, block_m, block_n);
   return FA_OK;
 }
 
