@@ -1003,15 +1003,15 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
 // Host side
 // ------------------------------------------------------------------------------------
 
-// Compiled tile shapes: block_m query rows per workgroup (NW waves, each owning 32
-// query rows) and block_n keys per K/V tile, and the head sizes each is built for.
-// fa_fwd_kernel runs (64, 64), (128, 64) and (128, 32) at d = 64; fa_fwd_pipe_kernel
-// runs (128, 32) at d = 128 and the eight-wave tiles (256, 32 at d = 128 only: a
-// d = 64 tile of 32 keys is four 1 KB loads, fewer than the eight waves).
-struct TileShape { int bm, bn, nw; bool d64, d128; };
+// Compiled tile shapes: block_m query rows per workgroup and block_n keys per K/V
+// tile, and the head sizes each is built for. fa_fwd_kernel runs (64, 64) with two
+// waves, (128, 64) and (128, 32) with four (32 query rows each) at both head sizes,
+// and (256, 32) at d = 64 with four waves of two 32-query blocks each (every K and V
+// fragment read from LDS feeds both blocks); fa_fwd_pipe_kernel runs (128, 32) at
+// d = 128 with four waves and the eight-wave tiles (256, 32) at d = 128 and (256, 64).
+struct TileShape { int bm, bn; bool d64, d128; };
 constexpr TileShape kTiles[] = {
-    {64, 64, 2, true, true}, {128, 64, 4, true, true}, {128, 32, 4, true, true},
-    {256, 32, 8, false, true}, {256, 64, 8, true, true}};
+    {64, 64, true, true}, {128, 64, true, true}, {128, 32, true, true}, {256, 32, true, true}, {256, 64, true, true}};
 
 template <int D, bool BF16>
 hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
@@ -1025,9 +1025,9 @@ hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, bool BF16, bool CAUSAL, int NW, int BN>
+template <int D, bool BF16, bool CAUSAL, int NW, int BN, int QB = 1>
 hipError_t launch_four_wave(const Params& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, NW, 1, BN>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, NW, QB, BN>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1046,8 +1046,10 @@ hipError_t launch_tile(const Params& p, int bm, int bn, hipStream_t stream) {
     if constexpr (D == 64) return launch_four_wave<D, BF16, CAUSAL, 4, 32>(p, stream);
     else return launch_pipelined<D, BF16, CAUSAL, 4, 32>(p, stream);
   }
-  if constexpr (D == 128)
-    if (bm == 256 && bn == 32) return launch_pipelined<D, BF16, CAUSAL, 8, 32>(p, stream);
+  if (bm == 256 && bn == 32) {
+    if constexpr (D == 64) return launch_four_wave<D, BF16, CAUSAL, 4, 32, 2>(p, stream);
+    else return launch_pipelined<D, BF16, CAUSAL, 8, 32>(p, stream);
+  }
   if (bm == 256 && bn == 64) return launch_pipelined<D, BF16, CAUSAL, 8, 64>(p, stream);
   return hipErrorInvalidValue;
 }
@@ -1086,11 +1088,22 @@ fa_status read_strides(const int64_t* st, int64_t H, int64_t N, int64_t d, int64
   return FA_OK;
 }
 
+// B H ceil(N / bm) >= need, without forming a product that could overflow.
+bool grid_reaches(int64_t B, int64_t H, int64_t N, int64_t bm, int64_t need) {
+  if (B <= 0 || H <= 0 || N <= 0) return false;
+  const int64_t slices = (B >= need || H >= need) ? need : B * H;
+  const int64_t per = N / bm + (N % bm != 0);      // row blocks per slice
+  return per >= need || slices >= (need + per - 1) / per;
+}
+
 void default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int* bm, int* bn) {
   // Measured on MI355X (interleaved tile sweeps per workload family):
   //  - short sequences: the smallest tile, so that more workgroups exist;
-  //  - d = 64: the four-wave kernel (one 32-query block per wave; causal row blocks of
-  //    uneven length balance better with small blocks): 64-key tiles for long
+  //  - d = 64: the four-wave kernel. Without a mask, two 32-query blocks per wave
+  //    (256 rows, 32-key tiles: the K and V fragments read from LDS serve both) where
+  //    that grid still gives every CU two workgroups (+2.4% to +3.5% at N = 2048 to
+  //    16384; with one per CU, -16%); otherwise one block per wave (causal row blocks
+  //    of uneven length balance better with small blocks): 64-key tiles for long
   //    non-causal sequences and for causal ones from N = 2048 (+10% at N = 2048,
   //    +17% at 8192), 32-key tiles otherwise; the pipelined kernel measured 3% slower
   //    at N = 4096 (the softmax's VALU work, not the overlap, sets the pace there);
@@ -1106,16 +1119,13 @@ void default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int* b
     *bm = 64;
     *bn = 64;
   } else if (d == 128) {
-    // B H ceil(N / 256) >= need, without forming a product that could overflow
-    const int64_t need = causal ? 512 : 256;
-    const int64_t slices = (B >= need || H >= need) ? need : (B > 0 && H > 0 ? B * H : 0);
-    const int64_t per = N / 256 + (N % 256 != 0);      // 256-row blocks per slice
-    const bool eight = N >= 4096 && slices > 0 && (per >= need || slices >= (need + per - 1) / per);
+    const bool eight = N >= 4096 && grid_reaches(B, H, N, 256, causal ? 512 : 256);
     *bm = eight ? 256 : 128;
     *bn = (!causal && N < 4096 && N > 256) ? 64 : 32;
   } else {
-    *bm = 128;
-    *bn = ((!causal && N > 256) || (causal && N > 1024)) ? 64 : 32;
+    const bool two_blocks = !causal && N > 256 && grid_reaches(B, H, N, 256, 512);
+    *bm = two_blocks ? 256 : 128;
+    *bn = two_blocks ? 32 : ((!causal && N > 256) || (causal && N > 1024)) ? 64 : 32;
   }
 }
 
@@ -1124,10 +1134,13 @@ void default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int* b
 // lane): the four-wave tiles run one wave per SIMD per workgroup, two workgroups
 // per CU at 160..256 registers and three for the 32-key tiles at d = 64 (147..160);
 // the 2-wave (64, 64) tile fits two waves per SIMD at d = 64 (4 per CU) but needs
-// more than 256 registers at d = 128 (2 per CU); an eight-wave workgroup fills a CU.
+// more than 256 registers at d = 128 (2 per CU); the four-wave (256, 32) tile at
+// d = 64 (two query blocks per wave, 255 registers) two per CU; an eight-wave
+// workgroup fills a CU.
 int wgs_per_cu(int bm, int bn, int64_t d) {
   if (bm == 64) return d == 64 ? 4 : 2;
   if (bm == 128) return (d == 64 && bn == 32) ? 3 : 2;
+  if (bm == 256 && bn == 32 && d == 64) return 2;
   return 1;
 }
 
