@@ -500,15 +500,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
 
   // Tile j reads K(j) from stage j%2 and V(j-1) from stage (j-1)%2 while the direct
   // loads fill K(j+1) into stage (j+1)%2 and V(j) into stage j%2.
+  // Without a causal mask the first iteration's loads (K(1), V(0)) start with K(0):
+  // one memory round trip before the first tile instead of two. That matters where
+  // every workgroup of the grid starts at once (n4096_d64_f16: +2.4%, N = 2048 and
+  // 8192: +1.1% to +1.3%); under the causal mask, whose workgroups start staggered,
+  // it measured 1-2% slower.
+  constexpr bool EARLY = !CAUSAL;
   auto full_tile = [&](int j, short* k_rd, short* k_wr, short* v_rd, short* v_wr, auto prev_tag) {
     const int n0 = kb + j * BN;
     sync_tile();
-    if (j + 1 < ntiles) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
-    issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
+    if (!EARLY || j > 0) {
+      if (j + 1 < ntiles) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
+      issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
+    }
     step(n0, k_rd, v_rd, std::false_type{}, prev_tag);
   };
   bool have_prev = false;   // pprev holds the weights of tile j-1 (wave-uniform)
-  if (ntiles > 0) issue_tile_load(rk, dma_off_k, p.k_sr, lds_k0, kb);
+  if (ntiles > 0) {
+    issue_tile_load(rk, dma_off_k, p.k_sr, lds_k0, kb);
+    if (EARLY) {
+      if (ntiles > 1) issue_tile_load(rk, dma_off_k, p.k_sr, lds_k1, kb + BN);
+      issue_tile_load(rv, dma_off_v, p.v_sr, lds_v0, kb);
+    }
+  }
   int j = 0;
   if (n_full > 0) {
     full_tile(0, lds_k0, lds_k1, lds_v1, lds_v0, std::false_type{});
@@ -530,8 +544,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     short* v_rd = (j & 1) ? lds_v0 : lds_v1;
     short* v_wr = (j & 1) ? lds_v1 : lds_v0;
     sync_tile();
-    if (j + 1 < ntiles) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
-    issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
+    if (!EARLY || j > 0) {
+      if (j + 1 < ntiles) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
+      issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
+    }
     if (CAUSAL && n0 > w_last_q + off) {   // whole tile in this wave's future
       if (have_prev) pv_outside(v_rd);
       have_prev = false;
