@@ -126,8 +126,9 @@ fa_status fa_fwd_tiled(const void* q, const void* k, const void* v, void* o, flo
  *             the one that differs from top-left only when the lengths differ): the
  *             last query sees every key. With Nq = Nk this is fa_fwd's mask. A query
  *             with no visible key (Nq > Nk, i < Nq - Nk) gets O = 0 and LSE = -inf.
- *   block_m, block_n: a compiled tile, or 0, 0 for the tile fa_fwd would choose for Nq
- *             (for the packed row count when grouped heads are packed, see below).
+ *   block_m, block_n: a compiled tile, or 0, 0 for the tile fa_fwd would choose for
+ *             B, Hq and Nq (for the packed row count when grouped heads are packed, see
+ *             below).
  *   Other arguments, ownership and errors as for fa_fwd; additionally
  *   FA_ERR_BAD_STRIDE. Nk = 0 is allowed (every row gets O = 0, LSE = -inf; k and v
  *   may then be NULL). B*Hq*Nq == 0 is a no-op.
