@@ -586,7 +586,7 @@ struct Interleave {
 };
 
 // ------------------------------------------------------------------------------------
-// Software-pipelined four-wave kernel
+// Software-pipelined kernel (four or eight waves)
 // ------------------------------------------------------------------------------------
 //
 // On gfx950 one wave issues a VALU instruction only every ~6 cycles while the SIMD's
@@ -649,24 +649,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   const int wq0 = m0 + wave * 32;
   const float c = p.c;
 
-  // LDS fragment offsets, as in fa_fwd_kernel
+  // LDS fragment offsets, as in fa_fwd_kernel, in bytes
   auto frag_offsets = [](int ln, int (&ko)[NKS], int (&vo)[NDB][2]) __attribute__((always_inline)) {
     const int r32 = ln & 31, h = ln >> 5;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) ko[ks] = r32 * D + (((2 * ks + h) ^ swz<D>(r32)) << 3);
+    for (int ks = 0; ks < NKS; ++ks) ko[ks] = 2 * (r32 * D + (((2 * ks + h) ^ swz<D>(r32)) << 3));
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int sec = 0; sec < 2; ++sec) {
         const int r = 4 * h + ((ln & 15) >> 2) + 8 * sec;
         const int ch = 4 * db + 2 * ((ln >> 4) & 1) + ((ln & 3) >> 1);
-        vo[db][sec] = r * D + ((ch ^ swz<D>(r)) << 3) + 4 * (ln & 1);
+        vo[db][sec] = 2 * (r * D + ((ch ^ swz<D>(r)) << 3) + 4 * (ln & 1));
       }
   };
-  // With every operand of a 64-key tile live at d = 128 the loop would spill; there
-  // the offsets are recomputed per tile from a copy of the lane index the compiler
-  // cannot hoist (248 registers, no spill).
-  constexpr bool RECOMP = D == 128 && BN == 64;
   int koff[NKS], voff[NDB][2];
   frag_offsets(lane, koff, voff);
   uint32_t dma_off_k[PATS], dma_off_v[PATS];
@@ -719,15 +715,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   // i-th MFMA of S = K Q^T (kb fastest, so that consecutive MFMAs are independent)
   auto qk_mfma = [&](f32x16 (&s)[NKB], const short* kbuf, int i, const int (&ko)[NKS]) __attribute__((always_inline)) {
     const int ks = i / NKB, kbk = i % NKB;
-    const i16x8 a = *(const i16x8*)(kbuf + kbk * 32 * D + ko[ks]);
+    const i16x8 a = *(const i16x8*)((const char*)(kbuf + kbk * 32 * D) + ko[ks]);
     s[kbk] = mfma_32x32x16<BF16>(a, qf[ks], ks == 0 ? f32x16{} : s[kbk]);
   };
   // i-th MFMA of U += V^T P^T (db fastest)
   auto pv_mfma = [&](const i16x8 (&pw)[NTT], const short* vbuf, int i, const int (&vo)[NDB][2]) __attribute__((always_inline)) {
     const int tt = i / NDB, db = i % NDB;
     const short* src = vbuf + ((tt >> 1) * 32 + 16 * (tt & 1)) * D;
-    const i16x4 a0 = ds_read_tr16(src + vo[db][0]);
-    const i16x4 a1 = ds_read_tr16(src + vo[db][1]);
+    const i16x4 a0 = ds_read_tr16((const short*)((const char*)src + vo[db][0]));
+    const i16x4 a1 = ds_read_tr16((const short*)((const char*)src + vo[db][1]));
     acc_o[db] = mfma_32x32x16<BF16>(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), pw[tt], acc_o[db]);
   };
   // weights of 16 keys (chunk tt) of s against the current reference, packed into pw[tt];
@@ -789,14 +785,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   auto body = [&](f32x16 (&s_cur)[NKB], f32x16 (&s_next)[NKB], i16x8 (&p_cur)[NTT], const i16x8 (&p_prev)[NTT],
                   const short* kbuf, const short* vbuf, int n0, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    int ko_f[NKS], vo_f[NDB][2];
-    if constexpr (RECOMP) {
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      frag_offsets(ln, ko_f, vo_f);
-    }
-    const int(&ko)[NKS] = RECOMP ? ko_f : koff;
-    const int(&vo)[NDB][2] = RECOMP ? vo_f : voff;
+    // The offsets pass through an empty asm once per tile, so the compiler cannot
+    // hoist offset + stage address out of the loop: each stage's address then folds
+    // into the reads' offset field, where hoisted sums would hold NKS + 2 * NDB
+    // registers per stage (at d = 128 with 64-key tiles the loop would spill).
+    // Not volatile, so that the asm does not split the scheduling region.
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) asm("" : "+v"(koff[i]));
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) asm("" : "+v"(voff[i][h]));
+    const int(&ko)[NKS] = koff;
+    const int(&vo)[NDB][2] = voff;
     if constexpr (MASK) apply_mask(s_cur, n0);
     float part[2];
 #pragma unroll
@@ -1057,7 +1058,10 @@ hipError_t launch_pipelined(const Params& p, hipStream_t stream) {
 template <int D, bool BF16, bool CAUSAL>
 hipError_t launch_tile(const Params& p, int bm, int bn, hipStream_t stream) {
   if (bm == 64 && bn == 64) return launch_four_wave<D, BF16, CAUSAL, 2, 64>(p, stream);
-  if (bm == 128 && bn == 64) return launch_four_wave<D, BF16, CAUSAL, 4, 64>(p, stream);
+  if (bm == 128 && bn == 64) {
+    if constexpr (D == 64) return launch_four_wave<D, BF16, CAUSAL, 4, 64>(p, stream);
+    else return launch_pipelined<D, BF16, CAUSAL, 4, 64>(p, stream);
+  }
   if (bm == 128 && bn == 32) {
     if constexpr (D == 64) return launch_four_wave<D, BF16, CAUSAL, 4, 32>(p, stream);
     else return launch_pipelined<D, BF16, CAUSAL, 4, 32>(p, stream);
@@ -1123,21 +1127,22 @@ void default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int* b
   //    non-causal sequences and for causal ones from N = 2048 (+10% at N = 2048,
   //    +17% at 8192), 32-key tiles otherwise; the pipelined kernel measured 3% slower
   //    at N = 4096 (the softmax's VALU work, not the overlap, sets the pace there);
-  //  - d = 128: the pipelined kernel with 32-key tiles, four waves under a causal mask
-  //    (+1.7% at N = 2048 against the four-wave kernel) and eight waves for long
-  //    sequences (+1.7% to +2.3% at N = 16384 without a mask, +1.5% to +3.2% at
-  //    N = 4096 to 16384 with one: one workgroup of 256 rows per CU streams each K/V
-  //    tile once for twice the rows), provided the 256-row grid covers the 256 CUs
-  //    (without a mask) or twice that (with one, whose row blocks differ in length):
-  //    below that the 128-row tile was 19% to 35% faster (N = 4096 and 8192, 8 heads);
-  //    (128, 64) in between.
+  //  - d = 128: the pipelined kernel. Eight waves for long sequences (one workgroup
+  //    of 256 rows per CU streams each K/V tile once for twice the rows: +1.7% to
+  //    +2.3% at N = 16384 without a mask, +1.5% to +3.2% at N = 4096 to 16384 with
+  //    one), provided the 256-row grid covers the 256 CUs (without a mask) or twice
+  //    that (with one, whose row blocks differ in length): below that the 128-row tile
+  //    was 19% to 35% faster (N = 4096 and 8192, 8 heads). 64-key tiles from N = 4096
+  //    (+2.3% to +5% over 32-key ones with 256 rows, +3.4% to +8.3% with 128) and for
+  //    shorter sequences without a mask (within 1% of the 32-key and four-wave tiles);
+  //    32-key tiles for shorter causal ones (+1.2% at N = 2048).
   if (N <= 128) {
     *bm = 64;
     *bn = 64;
   } else if (d == 128) {
     const bool eight = N >= 4096 && grid_reaches(B, H, N, 256, causal ? 512 : 256);
     *bm = eight ? 256 : 128;
-    *bn = (!causal && N < 4096 && N > 256) ? 64 : 32;
+    *bn = (N >= 4096 || (!causal && N > 256)) ? 64 : 32;
   } else {
     const bool two_blocks = !causal && N > 256 && grid_reaches(B, H, N, 256, 512);
     *bm = two_blocks ? 256 : 128;

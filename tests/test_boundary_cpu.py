@@ -53,15 +53,17 @@ def test_tile_queries():
 
 
 @pytest.mark.parametrize("B,H,N,causal,tile", [
-    (1, 16, 16384, False, (256, 32)),   # 1024 blocks of 256 rows: eight waves
-    (1, 16, 4096, False, (256, 32)),    # 256 blocks: one per CU
-    (1, 8, 4096, False, (128, 32)),     # 128 blocks of 256 rows would leave half the CUs idle
-    (2, 16, 4096, True, (256, 32)),     # causal: 512 blocks
-    (1, 16, 8192, True, (256, 32)),
-    (1, 8, 8192, True, (128, 32)),      # causal: 256 blocks of uneven length are too few
+    (1, 16, 16384, False, (256, 64)),   # 1024 blocks of 256 rows: eight waves, 64-key tiles
+    (1, 16, 4096, False, (256, 64)),    # 256 blocks: one per CU
+    (1, 8, 4096, False, (128, 64)),     # 128 blocks of 256 rows would leave half the CUs idle
+    (2, 16, 4096, True, (256, 64)),     # causal: 512 blocks
+    (1, 16, 8192, True, (256, 64)),
+    (1, 8, 8192, True, (128, 64)),      # causal: 256 blocks of uneven length are too few
+    (2, 16, 2048, False, (128, 64)),
+    (2, 16, 256, False, (128, 32)),
     (4, 32, 2048, True, (128, 32)),     # short rows: 128-row blocks
-    (1, 1, 1 << 40, True, (256, 32)),   # sizes far past any real grid: no overflow
-    (1 << 40, 1 << 40, 4096, False, (256, 32)),
+    (1, 1, 1 << 40, True, (256, 64)),   # sizes far past any real grid: no overflow
+    (1 << 40, 1 << 40, 4096, False, (256, 64)),
 ])
 def test_default_tile_d128_follows_the_grid(B, H, N, causal, tile):
     """At d = 128 the eight-wave 256-row tile is chosen only when its grid covers the CUs
