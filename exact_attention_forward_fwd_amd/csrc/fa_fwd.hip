@@ -261,14 +261,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
         vo[db][sec] = r * D + ((ch ^ swz<D>(r)) << 3) + 4 * (ln & 1);
       }
   };
-  // The offsets normally stay in registers for the whole loop. In the d = 128 causal
-  // variant, whose loop otherwise spills (the accumulators, Q^T and the previous
-  // tile's weights take most of 256 registers), they are recomputed where they are
-  // used (one XOR and shift each) from a copy of the lane index the compiler cannot
-  // hoist out of the loop (measured 449 -> 775 TFLOP/s); the other variants do not
-  // spill in their main loop and only lose by the extra VALU work. The non-causal
-  // d = 128 variant recomputes them in its masked tiles (the ragged last tile) only,
-  // where the mask's registers made it spill (N = 1000, B = 8, H = 32: 683 -> 825).
+  // The offsets normally stay in registers for the whole loop. At d = 128 (where this
+  // kernel runs the two-wave (64, 64) tile; the four-wave tiles there belong to the
+  // pipelined kernel) the causal variant's loop otherwise spills (the accumulators,
+  // Q^T and the previous tile's weights take most of 256 registers), so the offsets
+  // are recomputed where they are used (one XOR and shift each) from a copy of the
+  // lane index the compiler cannot hoist out of the loop (measured on the four-wave
+  // (128, 64) tile: 449 -> 775 TFLOP/s); the other variants do not spill in their
+  // main loop and only lose by the extra VALU work. The non-causal d = 128 variant
+  // recomputes them in its masked tiles (the ragged last tile) only, where the mask's
+  // registers made it spill (N = 1000, B = 8, H = 32: 683 -> 825).
   constexpr bool RECOMPUTE_OFFSETS = D == 128 && CAUSAL;
   constexpr bool RECOMPUTE_MASKED = RECOMPUTE_OFFSETS || (D == 128 && !CAUSAL && BN == 64);
   int koff_live[D / 16], voff_live[D / 32][2];
@@ -1022,10 +1024,11 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
 
 // Compiled tile shapes: block_m query rows per workgroup and block_n keys per K/V
 // tile, and the head sizes each is built for. fa_fwd_kernel runs (64, 64) with two
-// waves, (128, 64) and (128, 32) with four (32 query rows each) at both head sizes,
-// and (256, 32) at d = 64 with four waves of two 32-query blocks each (every K and V
-// fragment read from LDS feeds both blocks); fa_fwd_pipe_kernel runs (128, 32) at
-// d = 128 with four waves and the eight-wave tiles (256, 32) at d = 128 and (256, 64).
+// waves at both head sizes, (128, 64) and (128, 32) with four (32 query rows each)
+// at d = 64, and (256, 32) at d = 64 with four waves of two 32-query blocks each
+// (every K and V fragment read from LDS feeds both blocks); fa_fwd_pipe_kernel runs
+// (128, 64) and (128, 32) at d = 128 with four waves and the eight-wave tiles
+// (256, 32) at d = 128 and (256, 64) at both.
 struct TileShape { int bm, bn; bool d64, d128; };
 constexpr TileShape kTiles[] = {
     {64, 64, true, true}, {128, 64, true, true}, {128, 32, true, true}, {256, 32, true, true}, {256, 64, true, true}};
@@ -1152,8 +1155,9 @@ void default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int* b
 
 
 // Resident workgroups per CU, from each tile's registers (a SIMD holds 512 per
-// lane): the four-wave tiles run one wave per SIMD per workgroup, two workgroups
-// per CU at 160..256 registers and three for the 32-key tiles at d = 64 (147..160);
+// lane): the four-wave tiles of both kernels run one wave per SIMD per workgroup,
+// two workgroups per CU at 169..256 registers and three for the 32-key tiles at
+// d = 64 (at most 168);
 // the 2-wave (64, 64) tile fits two waves per SIMD at d = 64 (4 per CU) but needs
 // more than 256 registers at d = 128 (2 per CU); the four-wave (256, 32) tile at
 // d = 64 (two query blocks per wave, 255 registers) two per CU; an eight-wave

@@ -23,8 +23,9 @@ TOL_O = {"f16": 2e-3, "bf16": 1e-2}
 TOL_LSE = 1e-3
 TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16}
 ALL_TILES = [(64, 64), (128, 64), (128, 32), (256, 32), (256, 64)]
-# eight-wave tiles (256 query rows per workgroup, two waves per SIMD)
-PP_TILES = [(256, 32), (256, 64)]
+# tiles of the software-pipelined kernel at d = 128 (all of them) and of the 256-row
+# workgroups at d = 64
+PP_TILES = [(128, 32), (128, 64), (256, 32), (256, 64)]
 
 
 def _say(msg):
@@ -185,8 +186,8 @@ def test_every_tile_shape(tile, d):
 @pytest.mark.parametrize("tile", PP_TILES)
 @pytest.mark.parametrize("d", [64, 128])
 def test_pp_tiles_edge_sizes(N, tile, d):
-    """The eight-wave tiles at sizes where a workgroup has one, two or three key tiles,
-    waves whose rows start past N, and ragged last tiles."""
+    """The pipelined and 256-row tiles at sizes where a workgroup has one, two or three
+    key tiles, waves whose rows start past N, and ragged last tiles."""
     if not fa.fa_tile_supported(d, *tile):
         pytest.skip(f"tile {tile} is not compiled for d={d}")
     for dtype in ("f16", "bf16"):
