@@ -45,6 +45,13 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run exact_attention_forward_fwd_amd.build.build() "
                            "(or __graft_entry__.build()) first")
+    # libfa.so must use the HIP runtime that torch (which owns the tensors and streams
+    # passed in) has loaded. torch ships its own libamdhip64 (file libamdhip64.so,
+    # soname libamdhip64.so.7). Loaded first, it satisfies libfa.so's dependency on
+    # libamdhip64.so.7; loaded after libfa.so, which would bring in the system runtime,
+    # it becomes a second runtime in the process, and the one libfa.so calls then
+    # finds no device (every launch returns FA_ERR_HIP).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     common = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, i32, i32, vp]

@@ -623,14 +623,15 @@ hipError_t launch_bwd(const BwdParams& p, bool causal, hipStream_t s) {
   // The dQ kernel writes -D and the base-2 LSE of every query row before the dK/dV
   // kernel reads them (stream order). dq_wgs is 0 only without query rows, dkdv_wgs
   // only without keys.
+  hipError_t e = hipSuccess;
   if (causal) {
-    if (p.dq_wgs > 0) hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, true>), dim3(p.dq_wgs), dim3(256), 0, s, p);
-    if (p.dkdv_wgs > 0) hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, true>), dim3(p.dkdv_wgs), dim3(256), 0, s, p);
+    if (p.dq_wgs > 0) e = launch_kernel(&fa_bwd_dq_kernel<D, BF16, true>, p.dq_wgs, 256, s, p);
+    if (e == hipSuccess && p.dkdv_wgs > 0) e = launch_kernel(&fa_bwd_dkdv_kernel<D, BF16, true>, p.dkdv_wgs, 256, s, p);
   } else {
-    if (p.dq_wgs > 0) hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16, false>), dim3(p.dq_wgs), dim3(256), 0, s, p);
-    if (p.dkdv_wgs > 0) hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16, false>), dim3(p.dkdv_wgs), dim3(256), 0, s, p);
+    if (p.dq_wgs > 0) e = launch_kernel(&fa_bwd_dq_kernel<D, BF16, false>, p.dq_wgs, 256, s, p);
+    if (e == hipSuccess && p.dkdv_wgs > 0) e = launch_kernel(&fa_bwd_dkdv_kernel<D, BF16, false>, p.dkdv_wgs, 256, s, p);
   }
-  return hipGetLastError();
+  return e;
 }
 
 // Shared by fa_bwd and fa_bwd_ex: contiguous [B, H, N, d] tensors, K/V heads shared by

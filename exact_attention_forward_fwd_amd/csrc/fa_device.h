@@ -1,7 +1,8 @@
 // Device helpers shared by the forward and backward kernels (gfx950 / CDNA4):
 // vector types, the 32x32x16 MFMA for fp16 and bf16, cross-half reductions, the
 // transposing LDS read, buffer resources with zero fill past the end, direct
-// memory-to-LDS loads and the XOR swizzle of K/V-style tiles in LDS.
+// memory-to-LDS loads, the XOR swizzle of K/V-style tiles in LDS, and the host-side
+// launch helper.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -15,6 +16,18 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLn2 = 0.6931471805599453f;
+
+// Launches kernel(arg) with `grid` workgroups of `block` threads on `stream` and
+// returns the status of this launch alone. (hipGetLastError after a <<<>>> launch
+// would also return, and clear, an error that an earlier, unrelated HIP call of the
+// caller's thread left pending: a successful launch would then be reported as failed,
+// and the caller's own error lost.)
+template <class P>
+inline hipError_t launch_kernel(void (*kernel)(P), int64_t grid, int block, hipStream_t stream, P arg) {
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)grid), dim3((unsigned)block), args,
+                         0, stream);
+}
 
 template <bool BF16> struct Elem;
 template <> struct Elem<false> { using vec8 = f16x8; };

@@ -1039,22 +1039,19 @@ hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
   // grid has enough workgroups and each lane fewer dependent load rounds.
   constexpr int RPB1 = 256 / (D / 4), RPB8 = RPB1 / 8;
   if ((m.rows + RPB1 - 1) / RPB1 < 512)
-    hipLaunchKernelGGL((fa_merge_kernel<D, BF16, 8>), dim3((m.rows + RPB8 - 1) / RPB8), dim3(256), 0, stream, m);
+    return launch_kernel(&fa_merge_kernel<D, BF16, 8>, (m.rows + RPB8 - 1) / RPB8, 256, stream, m);
   else
-    hipLaunchKernelGGL((fa_merge_kernel<D, BF16, 1>), dim3((m.rows + RPB1 - 1) / RPB1), dim3(256), 0, stream, m);
-  return hipGetLastError();
+    return launch_kernel(&fa_merge_kernel<D, BF16, 1>, (m.rows + RPB1 - 1) / RPB1, 256, stream, m);
 }
 
 template <int D, bool BF16, bool CAUSAL, int NW, int BN, int QB = 1>
 hipError_t launch_four_wave(const Params& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, CAUSAL, NW, QB, BN>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(&fa_fwd_kernel<D, BF16, CAUSAL, NW, QB, BN>, p.total_wgs, NW * 64, stream, p);
 }
 
 template <int D, bool BF16, bool CAUSAL, int NW, int BN>
 hipError_t launch_pipelined(const Params& p, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_pipe_kernel<D, BF16, CAUSAL, NW, BN>), dim3(p.total_wgs), dim3(NW * 64), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(&fa_fwd_pipe_kernel<D, BF16, CAUSAL, NW, BN>, p.total_wgs, NW * 64, stream, p);
 }
 
 // The launch for a tile of kTiles (tile_ok has accepted it for this D).

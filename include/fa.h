@@ -49,7 +49,8 @@ typedef enum {
   FA_ERR_MISALIGNED = 6,         /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_TOO_LARGE = 7,          /* (N + 512) * row stride >= 2^30 elements, B * H * N >= 2^31, or the grid exceeds 2^31-1 workgroups */
   FA_ERR_UNSUPPORTED_TILE = 8,   /* (block_m, block_n) not among the compiled tile shapes */
-  FA_ERR_HIP = 9,                /* the HIP runtime reported an error at launch */
+  FA_ERR_HIP = 9,                /* the HIP runtime refused a launch of this call (that launch's own status;
+                                    an error pending from an earlier HIP call of the thread is left as it was) */
   FA_ERR_BAD_STRIDE = 10,        /* a stride is negative or not a multiple of 8 elements, or a row stride < d */
   FA_ERR_BAD_SPLITS = 11,        /* num_splits outside [1, 256] */
   FA_ERR_WORKSPACE = 12,         /* workspace (split-KV or backward) NULL, not 16-byte aligned or too small */

@@ -224,6 +224,68 @@ def test_side_stream_and_repeat_determinism():
     np.testing.assert_array_equal(l1, l2)
 
 
+def test_pending_hip_error_of_the_caller_is_neither_reported_nor_cleared():
+    """A HIP error that an earlier, unrelated call of the caller's thread left pending
+    (here hipSetDevice with an ordinal no machine has) must not turn a successful
+    launch into FA_ERR_HIP, and must still be pending afterwards. Covers the forward,
+    the split-KV forward (two launches) and the backward (two launches)."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipSetDevice.restype = ctypes.c_int
+    hip.hipGetLastError.restype = ctypes.c_int
+    hip.hipPeekAtLastError.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    q, k, v = make_random(1, 2, 300, 128, "bf16", seed=91)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o_b, l_b = fa.fwd(qd, kd, vd, causal=True)
+    dout = torch.randn(qd.shape, generator=torch.Generator("cpu").manual_seed(92)).to(qd.dtype).to(dev)
+    calls = [
+        ("fwd", lambda: fa.fwd(qd, kd, vd, causal=True)),
+        ("fwd_split", lambda: fa.fwd_split(qd, kd, vd, causal=True, num_splits=3)),
+        ("bwd", lambda: fa.bwd(qd, kd, vd, o_b, dout, l_b, causal=True)),
+    ]
+    ref_o, ref_l = oracle.attention_fwd(f64(q), f64(k), f64(v), 1 / math.sqrt(128), True)
+    for name, call in calls:
+        hip.hipGetLastError()                     # start from a clean state
+        st = hip.hipSetDevice(1 << 20)            # fails on the host, touches no device
+        assert st != 0, "an out-of-range device ordinal was accepted"
+        out = call()                              # raises FaError on any status but FA_OK
+        torch.cuda.synchronize()
+        assert hip.hipGetLastError() == st, f"{name}: the caller's pending error was cleared or replaced"
+        if name != "bwd":
+            o, lse = out
+            assert np.abs(o.float().cpu().double().numpy() - ref_o).max() <= TOL_O["bf16"]
+            assert np.abs(lse.cpu().double().numpy() - ref_l).max() <= TOL_LSE
+        _say(f"[pending-error] {name}: launched, caller's error {st} still pending")
+
+
+def test_library_loaded_before_torch_shares_its_runtime():
+    """In a fresh process that loads libfa.so before it has imported torch, the library
+    still runs on the HIP runtime torch uses (torch ships its own copy; two copies in
+    one process do not share the device), and a forward matches an fp32 CPU reference."""
+    import subprocess
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys\n"
+        f"sys.path.insert(0, {root!r})\n"
+        "import exact_attention_forward_fwd_amd as fa\n"
+        "assert 'torch' not in sys.modules\n"
+        "fa.load_library()\n"
+        "import torch\n"
+        "g = torch.Generator().manual_seed(5)\n"
+        "q, k, v = (torch.randn(1, 2, 200, 64, generator=g).half() for _ in range(3))\n"
+        "o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda())\n"
+        "ref = torch.softmax((q.float() @ k.float().transpose(-1, -2)) * 0.125, -1) @ v.float()\n"
+        "print(float((o.float().cpu() - ref).abs().max()))\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    err = float(r.stdout.strip().splitlines()[-1])
+    _say(f"[load-order] max |dO| = {err:.2e}")
+    assert err <= TOL_O["f16"]
+
+
 def test_invalid_arguments_return_status():
     dev = torch.device("cuda:0")
     q = torch.zeros((1, 1, 64, 64), dtype=torch.float16, device=dev)
