@@ -101,3 +101,38 @@ def test_noalloc_single_range_and_limit():
     torch.cuda.synchronize()
     assert rc == 13
     assert torch.isnan(o).all()
+
+
+def test_noalloc_captured_in_a_graph_replays_like_eager():
+    """The callers this entry point is for: capture one call (attention launch + merge
+    launch) in a HIP graph and replay it. Each replay, with eager work and a
+    synchronisation in between, must equal the eager call bit for bit; after the
+    inputs are overwritten in place, a replay must equal a fresh eager call on them."""
+    B, Hq, Hk, Nq, Nk, d = 1, 32, 8, 1, 16384, 128
+    q, k, v = _inputs(B, Hq, Hk, Nq, Nk, d, "bf16", seed=320)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    call = lambda: fa.fwd_split_noalloc(q, k, v, causal=True, num_splits=16, out=o, lse=lse)
+    call()                                   # eager; also looks up the scratch address
+    torch.cuda.synchronize()
+    o_ref, l_ref = o.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), f"replay {rep} differs from the eager call"
+        _say(f"[noalloc-graph] replay {rep} equals the eager call")
+    q2, k2, v2 = _inputs(B, Hq, Hk, Nq, Nk, d, "bf16", seed=321)
+    q.copy_(q2)
+    k.copy_(k2)
+    v.copy_(v2)
+    o_new, l_new = fa.fwd_split(q2, k2, v2, causal=True, num_splits=16)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_new) and torch.equal(lse, l_new)
