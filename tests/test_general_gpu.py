@@ -103,7 +103,7 @@ def _qkv(hq, hk, nq, nk, d, dtype, seed):
 @pytest.mark.parametrize("layouts", [("bnhd",) * 4, ("padded", "bnhd", "padded", "bhnd"),
                                      ("bhnd", "padded", "bnhd", "bnhd")], ids=["bnhd", "mixed1", "mixed2"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("tile", [None, (128, 32), (256, 32), (256, 64)])
+@pytest.mark.parametrize("tile", [None, (128, 32), (128, 64), (256, 32), (256, 64)])
 def test_strided_layouts(layouts, d, tile):
     if tile and not fa.fa_tile_supported(d, *tile):
         pytest.skip(f"tile {tile} is not compiled for d={d}")

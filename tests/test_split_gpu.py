@@ -86,7 +86,7 @@ def check_split(q, k, v, scale, causal, dtype, splits, tile=None, label="", ref=
                                    (300, 100)])
 @pytest.mark.parametrize("splits", [2, 3, 7, 64])
 def test_split_matches_oracle(nq, nk, splits):
-    for d, dtype, tiles in ((64, "f16", (None, (128, 64), (256, 64))), (128, "bf16", (None, (128, 32), (256, 32)))):
+    for d, dtype, tiles in ((64, "f16", (None, (128, 64), (256, 64))), (128, "bf16", (None, (128, 32), (128, 64), (256, 32), (256, 64)))):
         q, k, v = _qkv(2, 2, 2, nq, nk, d, dtype, seed=nq + 7 * nk + d + splits)
         for tile in tiles:
             for causal in (False, True):
