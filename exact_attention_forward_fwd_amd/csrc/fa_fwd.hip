@@ -1133,16 +1133,19 @@ void default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int* b
   //    one), provided the 256-row grid covers the 256 CUs (without a mask) or twice
   //    that (with one, whose row blocks differ in length): below that the 128-row tile
   //    was 19% to 35% faster (N = 4096 and 8192, 8 heads). 64-key tiles from N = 4096
-  //    (+2.3% to +5% over 32-key ones with 256 rows, +3.4% to +8.3% with 128) and for
-  //    shorter sequences without a mask (within 1% of the 32-key and four-wave tiles);
-  //    32-key tiles for shorter causal ones (+1.2% at N = 2048).
+  //    (+2.3% to +5% over 32-key ones with 256 rows, +3.4% to +8.3% with 128), for
+  //    shorter sequences without a mask (within 1% of the 32-key and four-wave tiles)
+  //    and for shorter causal ones whose 128-row grid is one round of two workgroups
+  //    per CU (+2.3% to +15% at N = 1024 to 3072); 32-key tiles for causal ones with
+  //    more workgroups than that (from -2.5% to +2% for 64 keys) and up to N = 256.
   if (N <= 128) {
     *bm = 64;
     *bn = 64;
   } else if (d == 128) {
     const bool eight = N >= 4096 && grid_reaches(B, H, N, 256, causal ? 512 : 256);
     *bm = eight ? 256 : 128;
-    *bn = (N >= 4096 || (!causal && N > 256)) ? 64 : 32;
+    const bool causal_rounds = causal && N < 4096 && grid_reaches(B, H, N, 128, 513);
+    *bn = (N > 256 && !causal_rounds) ? 64 : 32;
   } else {
     const bool two_blocks = !causal && N > 256 && grid_reaches(B, H, N, 256, 512);
     *bm = two_blocks ? 256 : 128;

@@ -61,7 +61,10 @@ def test_tile_queries():
     (1, 8, 8192, True, (128, 64)),      # causal: 256 blocks of uneven length are too few
     (2, 16, 2048, False, (128, 64)),
     (2, 16, 256, False, (128, 32)),
-    (4, 32, 2048, True, (128, 32)),     # short rows: 128-row blocks
+    (4, 32, 2048, True, (128, 32)),     # short rows: 128-row blocks; several rounds of them: 32-key tiles
+    (2, 16, 2048, True, (128, 64)),     # one round of 512 workgroups: 64-key tiles
+    (2, 16, 3072, True, (128, 32)),     # 768 workgroups
+    (1, 8, 200, True, (128, 32)),
     (1, 1, 1 << 40, True, (256, 64)),   # sizes far past any real grid: no overflow
     (1 << 40, 1 << 40, 4096, False, (256, 64)),
 ])
