@@ -1123,9 +1123,13 @@ void default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int* b
   //    (256 rows, 32-key tiles: the K and V fragments read from LDS serve both) where
   //    that grid still gives every CU two workgroups (+2.4% to +3.5% at N = 2048 to
   //    16384; with one per CU, -16%); otherwise one block per wave (causal row blocks
-  //    of uneven length balance better with small blocks): 64-key tiles for long
-  //    non-causal sequences and for causal ones from N = 2048 (+10% at N = 2048,
-  //    +17% at 8192), 32-key tiles otherwise; the pipelined kernel measured 3% slower
+  //    of uneven length balance better with small blocks): 64-key tiles for
+  //    non-causal sequences (+3.6% to +8% over 32-key ones at N = 1024 to 4096 with 8
+  //    or 16 heads); under a causal mask 64-key tiles (two workgroups per CU) while the
+  //    128-row grid is at most one round of 512 workgroups (+7.6% to +11% at N = 512 to
+  //    2048), or 1.5 rounds from N = 2048 (+11% at N = 3072), and 32-key tiles (three
+  //    workgroups per CU) beyond (64 keys: -9.4% to +0.2% at 1024 to 4096 workgroups,
+  //    except +4.5% at N = 8192 with 1024); the pipelined kernel measured 3% slower
   //    at N = 4096 (the softmax's VALU work, not the overlap, sets the pace there);
   //  - d = 128: the pipelined kernel. Eight waves for long sequences (one workgroup
   //    of 256 rows per CU streams each K/V tile once for twice the rows: +1.7% to
@@ -1149,7 +1153,15 @@ void default_tile(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int* b
   } else {
     const bool two_blocks = !causal && N > 256 && grid_reaches(B, H, N, 256, 512);
     *bm = two_blocks ? 256 : 128;
-    *bn = two_blocks ? 32 : ((!causal && N > 256) || (causal && N > 1024)) ? 64 : 32;
+    if (two_blocks || N <= 256) {
+      *bn = 32;
+    } else if (!causal) {
+      *bn = 64;
+    } else {
+      const bool one_round = !grid_reaches(B, H, N, 128, 513);
+      const bool rounds_and_half = N >= 2048 && !grid_reaches(B, H, N, 128, 769);
+      *bn = one_round || rounds_and_half ? 64 : 32;
+    }
   }
 }
 

@@ -74,6 +74,25 @@ def test_default_tile_d128_follows_the_grid(B, H, N, causal, tile):
     assert fa.fa_default_tile(B, H, N, 128, causal) == tile
 
 
+@pytest.mark.parametrize("B,H,N,causal,tile", [
+    (2, 16, 4096, False, (256, 32)),    # two query blocks per wave: 512 workgroups of 256 rows
+    (1, 16, 4096, False, (128, 64)),    # 256 of them would leave one per CU
+    (1, 8, 200, False, (128, 32)),
+    (8, 16, 1000, True, (128, 32)),     # 1024 causal row blocks: 32-key tiles, three per CU
+    (4, 32, 2048, True, (128, 32)),
+    (2, 16, 2048, True, (128, 64)),     # one round of 512: 64-key tiles
+    (4, 16, 1024, True, (128, 64)),
+    (4, 24, 1024, True, (128, 32)),     # 768 short rows
+    (2, 16, 3072, True, (128, 64)),     # 768 long rows: 1.5 rounds
+    (4, 16, 3072, True, (128, 32)),
+    (1, 8, 200, True, (128, 32)),
+])
+def test_default_tile_d64_follows_the_grid(B, H, N, causal, tile):
+    """At d = 64 the two-block tile needs two 256-row workgroups per CU; under a causal
+    mask the 64-key tile is chosen while its grid is about one round of 512."""
+    assert fa.fa_default_tile(B, H, N, 64, causal) == tile
+
+
 # Fake, aligned, never-dereferenced addresses: validation rejects before any launch.
 A = 0x10000
 
