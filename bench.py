@@ -23,6 +23,12 @@ import time
 MFMA_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk/CU (dense fp16/bf16) x 2.4 GHz
 HBM_PEAK_GBS = 8000.0
 HEADLINE = 2
+# From idle, back-to-back launches of one kernel speed up over the first ~30-50 ms of
+# device time before they reach a steady rate, which then holds (measured on MI355X:
+# n4096_d64_f16 167 -> 141 us per launch over the first ~250 launches, then 140-142 us
+# for 2.8 s, 20000 launches; n2048_d128_bf16_causal 186 -> 153 us). Every timing first
+# runs its call for this much device time, so that the timed steps see the steady rate.
+SETTLE_MS = 200.0
 
 
 def parse():
@@ -30,6 +36,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="before the warm-up steps of each timing, run the timed call back to back "
+                         "for at least this much device time (0: off); see settle()")
     ap.add_argument("--workload", type=int, default=HEADLINE, help="1..5 (default: the headline 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
@@ -151,6 +160,41 @@ def profile_mode(w, launches=3, backward=False):
           flush=True)
 
 
+def settle(call, stream, min_ms, steps):
+    """Runs `call` back to back in chunks of 16 until at least `min_ms` of device time has
+    passed (one chunk stays queued while the previous one is checked, so the device
+    never idles), then synchronises. Returns the launches and the device time. The
+    launch count is kept different from `steps`, so that a kernel trace can tell this
+    run from the timed one."""
+    import torch
+
+    if min_ms <= 0:
+        return {"launches": 0, "ms": 0.0}
+    chunk, n, total = 16, 0, 0.0
+    start = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    prev = start
+    pending = []
+    while True:
+        for _ in range(chunk):
+            call()
+        n += chunk
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        pending.append((prev, ev))
+        prev = ev
+        if len(pending) > 1:
+            a, b = pending.pop(0)
+            b.synchronize()
+            total += a.elapsed_time(b)
+            if (total >= min_ms and n != steps) or n >= 20000:
+                break
+    torch.cuda.synchronize()
+    for a, b in pending:
+        total += a.elapsed_time(b)
+    return {"launches": n, "ms": round(total, 1)}
+
+
 def time_calls(call, stream, steps):
     """Device time of `call` on `stream`. The timed region is `steps` back-to-back calls
     between one pair of HIP events recorded on that stream: its length / steps is the
@@ -181,7 +225,7 @@ def time_calls(call, stream, steps):
                 wall_ms=(wall1 - wall0) * 1e3)
 
 
-def time_workload(w, steps, warmup):
+def time_workload(w, steps, warmup, settle_ms=SETTLE_MS):
     import torch
     import exact_attention_forward_fwd_amd as fa
     from exact_attention_forward_fwd_amd.workloads import make_inputs
@@ -198,15 +242,16 @@ def time_workload(w, steps, warmup):
         fa.fwd(q, k, v, scale=w.scale, causal=w.causal, block_m=tile[0], block_n=tile[1],
                out=o, lse=lse, stream=stream)
 
+    sett = settle(step, stream, settle_ms, steps)
     for _ in range(warmup):
         step()
     # one launch per step: the step time is the kernel's average launch duration
     t = time_calls(step, stream, steps)
     return dict(ms_per_step=t["avg"], kernel_ms_avg=t["avg"], kernel_ms_median=t["median"],
-                kernel_ms_min=t["min"], wall_ms_per_step=t["wall_ms"] / steps, inputs=(q, k, v))
+                kernel_ms_min=t["min"], wall_ms_per_step=t["wall_ms"] / steps, settle=sett, inputs=(q, k, v))
 
 
-def time_split(w, steps, warmup):
+def time_split(w, steps, warmup, settle_ms=SETTLE_MS):
     """Per-call device time of fa_fwd_split (attention launch + merge launch) at the
     library's suggested split count, and of the unsplit call, on the same inputs: five
     alternating rounds of steps / 5 back-to-back calls each; call_ms_median is the
@@ -239,6 +284,7 @@ def time_split(w, steps, warmup):
 
     # the split and unsplit calls alternate in rounds, so that both see the same clock
     call_s, call_1 = caller(splits), caller(1)
+    settle(call_s, stream, settle_ms, steps)
     for _ in range(warmup):
         call_s()
         call_1()
@@ -266,7 +312,7 @@ def time_split(w, steps, warmup):
     return rec
 
 
-def time_backward(w, steps, warmup):
+def time_backward(w, steps, warmup, settle_ms=SETTLE_MS):
     """Per-call device time of fa_bwd (two launches: the dQ kernel, which also forms the
     row terms D = dO.O and the base-2 LSE, then the dK/dV kernel) on a forward benchmark
     workload with dO ~ N(0, 1), o and lse from fa_fwd. Algorithmic FLOPs are the five
@@ -295,6 +341,7 @@ def time_backward(w, steps, warmup):
         if rc != 0:
             raise fa.FaError(rc, "fa_bwd")
 
+    settle(call, stream, settle_ms, steps)
     for _ in range(warmup):
         call()
     t = time_calls(call, stream, steps)
@@ -397,7 +444,7 @@ def main():
     if args.profile:
         profile_mode(w, backward=args.backward)
         return
-    r = time_workload(w, args.steps, args.warmup)
+    r = time_workload(w, args.steps, args.warmup, args.settle_ms)
     tflops = w.flops / (r["ms_per_step"] * 1e-3) / 1e12
     achieved = w.flops / (r["kernel_ms_avg"] * 1e-3) / 1e12
     rec = stored_traffic(w)
@@ -410,6 +457,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"min_device_ms": args.settle_ms, "launches": r["settle"]["launches"],
+                   "device_ms": r["settle"]["ms"]},
         "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -436,7 +485,7 @@ def main():
             if idx == w.index:
                 continue
             wo = WORKLOADS[idx]
-            ro = time_workload(wo, max(5, args.steps // 5), max(2, args.warmup // 2))
+            ro = time_workload(wo, max(5, args.steps // 5), max(2, args.warmup // 2), args.settle_ms)
             tf = wo.flops / (ro["kernel_ms_avg"] * 1e-3) / 1e12
             others.append({"workload": wo.name, "dtype": wo.dtype, "causal": wo.causal,
                            "kernel_ms_avg": round(ro["kernel_ms_avg"], 5),
@@ -445,10 +494,11 @@ def main():
             torch.cuda.empty_cache()
         out["other_workloads"] = others
         from exact_attention_forward_fwd_amd.workloads import SPLIT_WORKLOADS
-        out["split_kv"] = [time_split(ws, max(10, args.steps // 2), max(3, args.warmup // 2))
+        out["split_kv"] = [time_split(ws, max(10, args.steps // 2), max(3, args.warmup // 2), args.settle_ms)
                            for ws in SPLIT_WORKLOADS.values()]
         torch.cuda.empty_cache()
-        out["backward"] = [time_backward(WORKLOADS[i], max(5, args.steps // 5), max(2, args.warmup // 2))
+        out["backward"] = [time_backward(WORKLOADS[i], max(5, args.steps // 5), max(2, args.warmup // 2),
+                                         args.settle_ms)
                            for i in (2, 4, 3)]
         torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
