@@ -206,6 +206,44 @@ def test_large_scores_rescaling():
     check_against_oracle(q, k, v, 0.5, True, "f16", label="large scores causal")
 
 
+def _one_tile_rows(dtype, N=256, d=64, seed=41):
+    """Inputs whose every row has its softmax mass in one 32-key group: row i's query
+    is A e_(i mod 8) and the keys of group t are B u_j e_t (u_j in [0.85, 1]), so with
+    scale 1/8 and A B / 8 = 20 a row scores 17..20 on its own group and 0 elsewhere
+    (weights e^-3 .. 1 against e^-20): l is, to 1e-7, the sum over one tile."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    A = B = math.sqrt(160.0)
+    q = torch.zeros(1, 4, N, d)
+    k = torch.zeros(1, 4, N, d)
+    rows = torch.arange(N)
+    q[0, :, rows, rows % 8] = A
+    u = 0.85 + 0.15 * torch.rand(4, N, generator=g)
+    k[0, :, rows, (rows // 32) % 8] = B * u
+    v = torch.randn(1, 4, N, d, generator=g)
+    dt = TORCH_DT[dtype]
+    return q.to(dt), k.to(dt), v.to(dt)
+
+
+@pytest.mark.parametrize("tile", [None, (128, 64), (256, 32), (64, 64)])
+def test_row_sums_of_one_tile_stay_within_their_bound(tile):
+    """fp16 weights in unmasked tiles are summed as rounded fp16 values by two levels
+    of packed adds; a lane's tile sum is then within 3 * 2^-12 = 7.3e-4 of the exact
+    sum, relative, and where one tile holds a row's mass that is LSE's error (plus
+    fp32 rounding). bf16 weights keep fp32 sums: there LSE is exact to fp32 rounding."""
+    q, k, v = _one_tile_rows("f16")
+    _, lse = check_against_oracle(q, k, v, 0.125, False, "f16", tile=tile, label="one-tile rows f16")
+    _, lse_ref = oracle.attention_fwd(f64(q), f64(k), f64(v), 0.125, False)
+    err = np.abs(lse - lse_ref).max()
+    _say(f"[rowsum] f16 tile {tile}: max|dLSE| = {err:.3e} against the bound 7.3e-4")
+    assert err <= 3 * 2.0 ** -12 + 1e-5
+    q, k, v = _one_tile_rows("bf16")
+    _, lse = check_against_oracle(q, k, v, 0.125, False, "bf16", tile=tile, label="one-tile rows bf16")
+    _, lse_ref = oracle.attention_fwd(f64(q), f64(k), f64(v), 0.125, False)
+    err = np.abs(lse - lse_ref).max()
+    _say(f"[rowsum] bf16 tile {tile}: max|dLSE| = {err:.3e}")
+    assert err <= 2e-5
+
+
 def test_empty_problems_are_noops():
     dev = torch.device("cuda:0")
     for shape in [(0, 2, 16, 64), (2, 0, 16, 64), (2, 2, 0, 64)]:
