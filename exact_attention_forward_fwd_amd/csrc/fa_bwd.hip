@@ -295,6 +295,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  // At d = 64 the dP accumulation starts from -D (a block of 16 registers that stays
+  // for the whole loop, the C operand of each tile's first dP MFMA), so that the MFMAs
+  // yield dP - D and dS = P (dP - D) is one multiply per score; at d = 128 those 16
+  // registers do not fit, and dS takes a subtraction as well.
+  constexpr bool DP_MINUS_D = D == 64;
+  f32x16 dp0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dp0[r] = DP_MINUS_D ? -dl : 0.f;
 
   const int n_end = CAUSAL ? max(0, min(Nk, m0 + BM + off)) : Nk;
   const int ntiles = (n_end + BN - 1) / BN;
@@ -311,13 +319,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   auto step = [&](int n0, const short* kbuf, const short* vbuf, bool mask) __attribute__((always_inline)) {
     f32x16 s, dp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
-#pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const i16x8 a = *(const i16x8*)(kbuf + rowf[ks]);
       const i16x8 b = *(const i16x8*)(vbuf + rowf[ks]);
-      s = mfma_32x32x16<BF16>(a, qf[ks], s);
-      dp = mfma_32x32x16<BF16>(b, dof[ks], dp);
+      s = mfma_32x32x16<BF16>(a, qf[ks], ks == 0 ? f32x16{} : s);
+      dp = mfma_32x32x16<BF16>(b, dof[ks], ks == 0 ? dp0 : dp);
     }
     // s[r], dp[r]: key n0 + 8 (r / 4) + 4 hi + r % 4, query qrow
     // The mask is applied to the whole tile behind one wave-uniform branch: a block
@@ -335,7 +341,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
     }
     float ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (dp[r] - dl);
+    for (int r = 0; r < 16; ++r) ds[r] = DP_MINUS_D ? pr[r] * dp[r] : pr[r] * (dp[r] - dl);
     i16x8 dsp[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {

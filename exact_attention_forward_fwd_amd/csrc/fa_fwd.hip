@@ -270,6 +270,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   const int l32 = lane & 31, hi = lane >> 5;
   const int wq0 = m0 + wave * 32 * QB;     // first query of this wave
   const float c = p.c;
+  // 1.0 kept out of the compiler's sight, so that x * one + sum with an fp16 x stays one
+  // v_fma_mix_f32 instead of a conversion and an add
+  float one = 1.0f;
+  asm("" : "+s"(one));
 
   // ---- per-lane LDS offsets (elements) ----
   // K fragment (A operand of S^T = K Q^T): row 32 kb + l32, 16-byte chunk 2 ks + hi.
@@ -504,25 +508,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
           e16x2 q4[BN / 16];
 #pragma unroll
           for (int i = 0; i < BN / 16; ++i) q4[i] = (pairs[4 * i] + pairs[4 * i + 1]) + (pairs[4 * i + 2] + pairs[4 * i + 3]);
-          // then into fp32: the first pair converted, each further half added by a
-          // mixed-precision FMA (half * 1 + sum), which issues as fast as an add, where
-          // a conversion and an add take two instructions (measured: +6% at N = 4096
-          // over starting the sums with FMAs into zero as well)
-          float acc[2] = {(float)q4[0].x, (float)q4[0].y};
+          // then into one fp32 sum by mixed-precision FMAs (half * 1 + sum, one
+          // v_fma_mix_f32 each, the first adding the two halves of a pair), which issue
+          // as fast as an add, where a conversion costs half as much again
+          float acc = __builtin_fmaf((float)q4[0].x, one, (float)q4[0].y);
 #pragma unroll
           for (int i = 1; i < BN / 16; ++i) {
-            asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "+v"(acc[0]) : "v"(q4[i]));
-            asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(acc[1]) : "v"(q4[i]));
+            acc = __builtin_fmaf((float)q4[i].x, one, acc);
+            acc = __builtin_fmaf((float)q4[i].y, one, acc);
           }
-          rs[qb] = acc[0] + acc[1];
+          rs[qb] = acc;
         }
       }
     };
     float rs[QB];
     weights(rs);
+    // After a full tile every row of the wave has a finite reference, so a full tile
+    // that follows one only checks the sums.
+    constexpr bool REF_SET = !MASK && HAVE_PREV;
     bool redo = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) redo |= !(rs[qb] <= kSumMax) || ref[qb] == -INFINITY;
+    for (int qb = 0; qb < QB; ++qb) redo |= !(rs[qb] <= kSumMax) || (!REF_SET && ref[qb] == -INFINITY);
     if (__builtin_amdgcn_ballot_w64(redo)) {   // wave-uniform: rare after the first tile
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
