@@ -499,7 +499,9 @@ def main():
             if idx == w.index:
                 continue
             wo = WORKLOADS[idx]
-            ro = time_workload(wo, max(5, args.steps // 5), max(2, args.warmup // 2), args.settle_ms)
+            # as many timed steps as the headline: a timed region of a few short launches
+            # (10 x 30 us) is stretched by the launch latency after its opening synchronisation
+            ro = time_workload(wo, args.steps, args.warmup, args.settle_ms)
             tf = wo.flops / (ro["kernel_ms_avg"] * 1e-3) / 1e12
             others.append({"workload": wo.name, "dtype": wo.dtype, "causal": wo.causal,
                            "kernel_ms_avg": round(ro["kernel_ms_avg"], 5),
@@ -508,11 +510,10 @@ def main():
             torch.cuda.empty_cache()
         out["other_workloads"] = others
         from exact_attention_forward_fwd_amd.workloads import SPLIT_WORKLOADS
-        out["split_kv"] = [time_split(ws, max(10, args.steps // 2), max(3, args.warmup // 2), args.settle_ms)
+        out["split_kv"] = [time_split(ws, args.steps, args.warmup, args.settle_ms)
                            for ws in SPLIT_WORKLOADS.values()]
         torch.cuda.empty_cache()
-        out["backward"] = [time_backward(WORKLOADS[i], max(5, args.steps // 5), max(2, args.warmup // 2),
-                                         args.settle_ms)
+        out["backward"] = [time_backward(WORKLOADS[i], args.steps, args.warmup, args.settle_ms)
                            for i in (2, 4, 3)]
         torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
