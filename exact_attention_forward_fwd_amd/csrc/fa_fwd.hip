@@ -140,14 +140,15 @@ constexpr float kSumMax = 256.0f;
 // Row sums of fp16 weights in unmasked tiles. Each lane's sum over a tile is formed
 // from the rounded weights (the values the second product multiplies): packed fp16
 // adds of pairs of pairs, so that each half sums four weights, then mixed-precision
-// FMAs into fp32. That is 11 instructions per 16 weights instead of 15 fp32 adds; a
-// wave's softmax runs at its instruction issue rate, so this is what counts (measured
-// +6.0% on B=2 H=16 N=4096 d=64, +5.6% and +6.4% at N = 2048 and 8192 without a mask,
-// +0.9% at N = 4096 under a causal mask, unchanged at N = 1000 causal). Each weight is
-// within 2^-12 of its fp32 value relative to it and each fp16 add rounds to 2^-12 of
-// its sum, so a tile's sum is within 3 * 2^-12 (7.3e-4) of the exact one, relative;
-// O = U / l is unaffected (U holds the same rounded weights) and LSE moves by at most
-// that much where one tile holds a row's mass, by far less where many tiles share it.
+// FMAs into one fp32 sum. That is 9 instructions per 16 weights instead of 15 fp32
+// adds; a wave's softmax runs at its instruction issue rate, so this is what counts
+// (measured +6.5% to +7% on B=2 H=16 N=4096 d=64 and at N = 2048 and 8192 without a
+// mask, +1.5% at N = 4096 under a causal mask, +0.5% at N = 1000 causal). Each weight
+// is within 2^-12 of its fp32 value relative to it and each fp16 add rounds to 2^-12
+// of its sum, so a tile's sum is within 3 * 2^-12 (7.3e-4) of the exact one, relative;
+// O = U / l is then the exact convex combination of the rounded weights U holds, and
+// LSE moves by at most that much where one tile holds a row's mass, by far less where
+// many tiles share it.
 // Masked tiles (the causal diagonal, the ragged end), where rows with few visible keys
 // have their mass, and bf16 weights (rounded to 2^-9) keep fp32 sums of the fp32 weights.
 constexpr bool kPackedSums = true;
