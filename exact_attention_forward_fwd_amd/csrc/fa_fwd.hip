@@ -404,6 +404,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
       }
     }
   };
+  // Read-ahead of V (one query block per wave at d = 64): K(j) and V(j) arrive together
+  // and share a stage index; each step reads its own V^T operands into registers at its
+  // end, and the next step's MFMA section opens with P V from those registers while its
+  // K reads are in flight, instead of waiting for LDS reads before its first MFMA.
+  // Outputs are bit-identical. Measured: +1.9% to +2.1% on causal d = 64 workloads
+  // (N = 1000 and 4096); with two query blocks per wave the operands do not fit beside
+  // the rest (-0.5%, spills when read earlier), so that tile keeps the in-step reads.
+  constexpr bool VPRE = D == 64 && QB == 1;
+  i16x8 vfr[D / 32][BN / 16];   // V^T operands of the previous tile (VPRE)
+  auto read_vfr = [&](const short* vbuf, const int (&voff)[D / 32][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int tt = 0; tt < BN / 16; ++tt) {
+        const short* src = vbuf + ((tt >> 1) * 32 + 16 * (tt & 1)) * D;
+        const i16x4 a0 = ds_read_tr16(src + voff[db][0]);
+        const i16x4 a1 = ds_read_tr16(src + voff[db][1]);
+        vfr[db][tt] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+  };
+  auto pv_regs = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int tt = 0; tt < BN / 16; ++tt)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc_o[qb][db] = mfma_32x32x16<BF16>(vfr[db][tt], pprev[qb][tt], acc_o[qb][db]);
+  };
   // P V outside a tile step (a causal tile in this wave's future, the last tile)
   auto pv_outside = [&](const short* vbuf) {
     if constexpr (RECOMPUTE_MASKED) {
@@ -429,6 +457,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     const int(&voff)[D / 32][2] = FRESH ? vo_new : voff_live;
     f32x16 s[QB][BN / 32];
     if constexpr (PRIO_ALL) __builtin_amdgcn_s_setprio(2);
+    if constexpr (VPRE && HAVE_PREV) pv_regs();
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
 #pragma unroll
@@ -443,7 +472,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
       }
     }
     // ---- the previous tile's P V: MFMA work that does not wait for this softmax ----
-    if constexpr (HAVE_PREV) {
+    if constexpr (HAVE_PREV && !VPRE) {
       if constexpr (kRaisePvPriority && !PRIO_ALL) __builtin_amdgcn_s_setprio(2);
       pv(vprev, voff);
     }
@@ -555,12 +584,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_run[qb] += rs[qb];
+    if constexpr (VPRE) read_vfr(vprev, voff);   // V(j) is in LDS since this tile's barrier
   };
 
   // LDS stores by other waves' direct loads become visible after this wave's own
   // loads have landed (vmcnt) and everyone has passed the barrier.
+  // With the read-ahead of V a wave's last V^T reads may still be in flight here; they
+  // complete before the barrier, after which other waves' loads overwrite that stage.
   auto sync_tile = [&]() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads are in LDS
+    if constexpr (VPRE)
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): also this wave's read-ahead of V
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads are in LDS
     __syncthreads();
   };
 
@@ -575,7 +610,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   auto full_tile = [&](int j, short* k_rd, short* k_wr, short* v_rd, short* v_wr, auto prev_tag) {
     const int n0 = kb + j * BN;
     sync_tile();
-    if (!EARLY || j > 0) {
+    if constexpr (VPRE) {
+      if ((!EARLY || j > 0) && j + 1 < ntiles) {
+        issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
+        issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0 + BN);
+      }
+    } else if (!EARLY || j > 0) {
       if (j + 1 < ntiles) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
       issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
     }
@@ -584,21 +624,31 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
   bool have_prev = false;   // pprev holds the weights of tile j-1 (wave-uniform)
   if (ntiles > 0) {
     issue_tile_load(rk, dma_off_k, p.k_sr, lds_k0, kb);
-    if (EARLY) {
+    if constexpr (VPRE) {
+      // K(j) and V(j) share a stage index: tile j reads both from stage j%2
+      issue_tile_load(rv, dma_off_v, p.v_sr, lds_v0, kb);
+      if (EARLY && ntiles > 1) {
+        issue_tile_load(rk, dma_off_k, p.k_sr, lds_k1, kb + BN);
+        issue_tile_load(rv, dma_off_v, p.v_sr, lds_v1, kb + BN);
+      }
+    } else if (EARLY) {
       if (ntiles > 1) issue_tile_load(rk, dma_off_k, p.k_sr, lds_k1, kb + BN);
       issue_tile_load(rv, dma_off_v, p.v_sr, lds_v0, kb);
     }
   }
   int j = 0;
+  // V stages: tile j reads V(j-1) from stage (j-1)%2, or with VPRE V(j) from stage j%2
+  short* const v_even_rd = VPRE ? lds_v0 : lds_v1;
+  short* const v_odd_rd = VPRE ? lds_v1 : lds_v0;
   if (n_full > 0) {
-    full_tile(0, lds_k0, lds_k1, lds_v1, lds_v0, std::false_type{});
+    full_tile(0, lds_k0, lds_k1, v_even_rd, v_odd_rd, std::false_type{});
     j = 1;
     for (; j + 1 < n_full; j += 2) {
-      full_tile(j, lds_k1, lds_k0, lds_v0, lds_v1, std::true_type{});
-      full_tile(j + 1, lds_k0, lds_k1, lds_v1, lds_v0, std::true_type{});
+      full_tile(j, lds_k1, lds_k0, v_odd_rd, v_even_rd, std::true_type{});
+      full_tile(j + 1, lds_k0, lds_k1, v_even_rd, v_odd_rd, std::true_type{});
     }
     if (j < n_full) {
-      full_tile(j, lds_k1, lds_k0, lds_v0, lds_v1, std::true_type{});
+      full_tile(j, lds_k1, lds_k0, v_odd_rd, v_even_rd, std::true_type{});
       ++j;
     }
     have_prev = true;
@@ -607,15 +657,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     const int n0 = kb + j * BN;
     short* k_rd = (j & 1) ? lds_k1 : lds_k0;
     short* k_wr = (j & 1) ? lds_k0 : lds_k1;
-    short* v_rd = (j & 1) ? lds_v0 : lds_v1;
-    short* v_wr = (j & 1) ? lds_v1 : lds_v0;
+    short* v_rd = (j & 1) ? v_odd_rd : v_even_rd;
+    short* v_wr = (j & 1) ? v_even_rd : v_odd_rd;
     sync_tile();
-    if (!EARLY || j > 0) {
+    if constexpr (VPRE) {
+      if ((!EARLY || j > 0) && j + 1 < ntiles) {
+        issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
+        issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0 + BN);
+      }
+    } else if (!EARLY || j > 0) {
       if (j + 1 < ntiles) issue_tile_load(rk, dma_off_k, p.k_sr, k_wr, n0 + BN);
       issue_tile_load(rv, dma_off_v, p.v_sr, v_wr, n0);
     }
     if (CAUSAL && n0 > w_last_q + off) {   // whole tile in this wave's future
-      if (have_prev) pv_outside(v_rd);
+      if (have_prev) {
+        if constexpr (VPRE) pv_regs();
+        else pv_outside(v_rd);
+      }
       have_prev = false;
       continue;
     }
@@ -623,8 +681,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WAVES_P
     else step(n0, k_rd, v_rd, std::true_type{}, std::false_type{});
     have_prev = true;
   }
-  sync_tile();                                  // V of the last tile is in LDS
-  if (have_prev) pv_outside(((ntiles - 1) & 1) ? lds_v1 : lds_v0);
+  if constexpr (VPRE) {
+    if (have_prev) pv_regs();                   // the last tile's V^T operands are in registers
+  } else {
+    sync_tile();                                // V of the last tile is in LDS
+    if (have_prev) pv_outside(((ntiles - 1) & 1) ? lds_v1 : lds_v0);
+  }
 
   // ---- epilogue: O = U / l, LSE = ln2 (ref + log2 l) ----
   write_rows<D, BF16, QB>(p, sl, bh, wi.split, wq0, lane, acc_o, ref, l_run);
