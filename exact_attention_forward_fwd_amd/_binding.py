@@ -43,8 +43,8 @@ def load_library(path: str = LIB_PATH):
     if _lib is not None and path == LIB_PATH:
         return _lib
     if not os.path.exists(path):
-        raise RuntimeError(f"{path} is not built; run exact_attention_forward_fwd_amd.build.build() "
-                           "(or __graft_entry__.build()) first")
+        raise RuntimeError(f"{path} is not built; run "
+                           "`python -m exact_attention_forward_fwd_amd.build` first")
     # libfa.so must use the HIP runtime that torch (which owns the tensors and streams
     # passed in) has loaded. torch ships its own libamdhip64 (file libamdhip64.so,
     # soname libamdhip64.so.7). Loaded first, it satisfies libfa.so's dependency on
