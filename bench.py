@@ -58,12 +58,14 @@ def parse():
 
 COPY_BYTES = 1 << 30   # 1 GiB read + 1 GiB written by the calibration copy
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_forward_fwd_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_device.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_forward_fwd_amd", *f) for f in
+                  (("csrc", "fa_fwd.hip"), ("csrc", "fa_device.h"), ("build.py",))]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash() -> str:
-    """SHA-256 over the forward kernels' sources (the kernel file and the device helpers it includes)."""
+    """SHA-256 over the forward kernels' sources (the kernel file, the device helpers it
+    includes and the build script, which holds the compiler options)."""
     import hashlib
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:

@@ -40,7 +40,12 @@
 #include "fa.h"
 #include "fa_device.h"
 
-namespace {
+// This file is compiled twice (build.py), with different instruction schedulers: as
+// a whole, and with FA_FWD_DEFAULT_SCHED_UNIT defined, when it holds only the launches
+// of the four-wave kernel under a causal mask and of its two-wave tiles (the kernels
+// that the maximum-ILP schedule slows down). The launch parameters cross between the
+// two units, so they live in a named namespace.
+namespace fa_fwd_unit {
 
 // One launch: B batches of Hq query heads; query head h reads K/V head h / group.
 // Tensors are [B, heads, rows, d] with arbitrary batch/head/row strides (elements)
@@ -71,6 +76,17 @@ struct Params {
   float* po;
   float* plse;
 };
+
+// Launch of fa_fwd_kernel<d, bf16, causal, nw, qb, bn> from the unit built with the
+// default scheduler; causal or nw == 2 only.
+hipError_t launch_default_sched(const Params& p, int d, bool bf16, bool causal, int nw, int bn, int qb,
+                                hipStream_t stream);
+
+}  // namespace fa_fwd_unit
+
+namespace {
+
+using fa_fwd_unit::Params;
 
 // Work item of a workgroup: slice (batch, query head), key range and query block.
 // The workgroups of one XCD take a contiguous range of items (dispatch is
@@ -1148,17 +1164,6 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams m) {
 // Host side
 // ------------------------------------------------------------------------------------
 
-// Compiled tile shapes: block_m query rows per workgroup and block_n keys per K/V
-// tile, and the head sizes each is built for. fa_fwd_kernel runs (64, 64) with two
-// waves at both head sizes, (128, 64) and (128, 32) with four (32 query rows each)
-// at d = 64, and (256, 32) at d = 64 with four waves of two 32-query blocks each
-// (every K and V fragment read from LDS feeds both blocks); fa_fwd_pipe_kernel runs
-// (128, 64) and (128, 32) at d = 128 with four waves and the eight-wave tiles
-// (256, 32) at d = 128 and (256, 64) at both.
-struct TileShape { int bm, bn; bool d64, d128; };
-constexpr TileShape kTiles[] = {
-    {64, 64, true, true}, {128, 64, true, true}, {128, 32, true, true}, {256, 32, true, true}, {256, 64, true, true}};
-
 template <int D, bool BF16>
 hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
   // Few rows (decoding): eight lane groups per row share its ranges, so that the
@@ -1172,7 +1177,10 @@ hipError_t launch_merge(const MergeParams& m, hipStream_t stream) {
 
 template <int D, bool BF16, bool CAUSAL, int NW, int BN, int QB = 1>
 hipError_t launch_four_wave(const Params& p, hipStream_t stream) {
-  return launch_kernel(&fa_fwd_kernel<D, BF16, CAUSAL, NW, QB, BN>, p.total_wgs, NW * 64, stream, p);
+  if constexpr (CAUSAL || NW == 2)
+    return fa_fwd_unit::launch_default_sched(p, D, BF16, CAUSAL, NW, BN, QB, stream);
+  else
+    return launch_kernel(&fa_fwd_kernel<D, BF16, CAUSAL, NW, QB, BN>, p.total_wgs, NW * 64, stream, p);
 }
 
 template <int D, bool BF16, bool CAUSAL, int NW, int BN>
@@ -1205,6 +1213,19 @@ hipError_t launch_d(const Params& p, bool bf16, bool causal, int bm, int bn, hip
   if (bf16) return causal ? launch_tile<D, true, true>(p, bm, bn, stream) : launch_tile<D, true, false>(p, bm, bn, stream);
   return causal ? launch_tile<D, false, true>(p, bm, bn, stream) : launch_tile<D, false, false>(p, bm, bn, stream);
 }
+
+#ifndef FA_FWD_DEFAULT_SCHED_UNIT
+
+// Compiled tile shapes: block_m query rows per workgroup and block_n keys per K/V
+// tile, and the head sizes each is built for. fa_fwd_kernel runs (64, 64) with two
+// waves at both head sizes, (128, 64) and (128, 32) with four (32 query rows each)
+// at d = 64, and (256, 32) at d = 64 with four waves of two 32-query blocks each
+// (every K and V fragment read from LDS feeds both blocks); fa_fwd_pipe_kernel runs
+// (128, 64) and (128, 32) at d = 128 with four waves and the eight-wave tiles
+// (256, 32) at d = 128 and (256, 64) at both.
+struct TileShape { int bm, bn; bool d64, d128; };
+constexpr TileShape kTiles[] = {
+    {64, 64, true, true}, {128, 64, true, true}, {128, 32, true, true}, {256, 32, true, true}, {256, 64, true, true}};
 
 bool tile_ok(int64_t d, int bm, int bn) {
   if (d != 64 && d != 128) return false;
@@ -1595,3 +1616,41 @@ const char* fa_status_str(fa_status status) {
 }
 
 }  // extern "C"
+
+#else  // FA_FWD_DEFAULT_SCHED_UNIT
+
+template <int D, bool BF16, bool CAUSAL, int NW, int BN, int QB>
+hipError_t launch_here(const Params& p, hipStream_t stream) {
+  return launch_kernel(&fa_fwd_kernel<D, BF16, CAUSAL, NW, QB, BN>, p.total_wgs, NW * 64, stream, p);
+}
+
+// The tiles launch_four_wave sends here: (64, 64) with two waves for either mask and
+// head size, and the d = 64 four-wave tiles under a causal mask.
+template <int D, bool BF16, bool CAUSAL>
+hipError_t launch_masked_or_two_wave(const Params& p, int nw, int bn, int qb, hipStream_t stream) {
+  if (nw == 2 && bn == 64 && qb == 1) return launch_here<D, BF16, CAUSAL, 2, 64, 1>(p, stream);
+  if constexpr (D == 64 && CAUSAL) {
+    if (nw == 4 && bn == 64 && qb == 1) return launch_here<64, BF16, true, 4, 64, 1>(p, stream);
+    if (nw == 4 && bn == 32 && qb == 1) return launch_here<64, BF16, true, 4, 32, 1>(p, stream);
+    if (nw == 4 && bn == 32 && qb == 2) return launch_here<64, BF16, true, 4, 32, 2>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t fa_fwd_unit::launch_default_sched(const Params& p, int d, bool bf16, bool causal, int nw, int bn, int qb,
+                                             hipStream_t stream) {
+  if (d == 64) {
+    if (bf16) return causal ? launch_masked_or_two_wave<64, true, true>(p, nw, bn, qb, stream)
+                            : launch_masked_or_two_wave<64, true, false>(p, nw, bn, qb, stream);
+    return causal ? launch_masked_or_two_wave<64, false, true>(p, nw, bn, qb, stream)
+                  : launch_masked_or_two_wave<64, false, false>(p, nw, bn, qb, stream);
+  }
+  if (bf16) return causal ? launch_masked_or_two_wave<128, true, true>(p, nw, bn, qb, stream)
+                          : launch_masked_or_two_wave<128, true, false>(p, nw, bn, qb, stream);
+  return causal ? launch_masked_or_two_wave<128, false, true>(p, nw, bn, qb, stream)
+                : launch_masked_or_two_wave<128, false, false>(p, nw, bn, qb, stream);
+}
+
+#endif  // FA_FWD_DEFAULT_SCHED_UNIT
